@@ -1,0 +1,261 @@
+"""Benchmark of the block-causal paged attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: build_tile_mask (tile
+classes, physical tile pages and the split-KV plan), attn_block_causal_paged, and
+kv_commit_block of the active blocks. Inputs are resident in HBM before timing starts.
+Before every timed step a 1 GiB buffer is overwritten so that neither L2 nor the 256 MB
+Infinity Cache still holds the KV cache (one layer's cache is cold when that layer runs
+again in a real decode step); HIP events bracket each step and each of its calls on the
+stream the kernels run on. A warm (no flush, back-to-back) figure is reported beside it.
+
+Prints one JSON line. `value` is microseconds per step (lower is better); `roofline`
+rates the dominant kernel (attention) against MI355X's HBM or bf16 matrix peak on
+algorithmic bytes/FLOPs; `cpu_baseline` is the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/decode-step + useful TFLOP/s & KV GB/s (% of MI355X roofline)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3
+# Which roof binds each workload (algorithmic FLOP/byte against the 314.6 FLOP/B ridge).
+BOUND = {1: "hbm", 2: "hbm", 3: "mfma", 4: "mfma", 5: "hbm"}
+KERNEL_SOURCES = ["attn_bf16.hip", "combine.hip"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2, help="workload number 1-5 (default 2)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
+    p.add_argument("--calib-copy", action="store_true", help="also run a plain copy kernel of known size")
+    return p.parse_args()
+
+
+def workload_stats(case):
+    """Useful FLOPs (4*d per visible (row, key, query head)) and algorithmic bytes."""
+    import numpy as np
+    d, Hq, Hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
+    esize = 2 if case.dtype == "bf16" else 4
+    visible = 0
+    for s in range(case.batch):
+        ql, kl = int(case.q_lens[s]), int(case.kv_len[s])
+        if case.q_blk is None:
+            i = np.arange(ql)
+            live = np.minimum(ql, (i // case.block_size + 1) * case.block_size)
+            visible += int((kl + live).sum())
+        else:
+            qb = np.sort(case.q_blk_seqs[s])
+            kb = np.sort(case.kv_blk_seqs[s])
+            rows = case.q_blk_seqs[s]
+            visible += int(np.searchsorted(kb, rows, side="right").sum()
+                           + np.searchsorted(qb, rows, side="right").sum())
+    flops = 4.0 * d * Hq * visible
+    cached_kv = float(case.kv_len.sum()) * Hkv * d * esize * 2
+    live_kv = float(case.total_q) * Hkv * d * esize * 2
+    q_o = float(case.total_q) * Hq * d * esize * 2
+    return flops, cached_kv, live_kv, q_o
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES + ["bcp_internal.h"]:
+        h.update(open(os.path.join(ROOT, "block_causal_paged_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(cfg):
+    """HBM bytes per attention call from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_traffic_C{cfg}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle as it stands, on whole sequences of the same workload until the budget is
+    spent; scaled to microseconds per full step by the fraction of query rows covered."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    order = list(range(case.batch))
+    t0 = time.perf_counter()
+    rows_done = 0
+    seqs = []
+    for s in order:
+        oracle.attention_rows(case.q, case.k_new, case.v_new, case.k_cache, case.v_cache, case.cu_q,
+                              case.kv_len, case.page_table, case.page_size, case.num_pages, s,
+                              block_size=case.block_size, q_blk=case.q_blk, kv_blk=case.kv_blk)
+        rows_done += int(case.q_lens[s])
+        seqs.append(s)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    frac = rows_done / max(1, case.total_q)
+    per_step_us = dt / frac * 1e6
+    return {"value": per_step_us, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"float64 NumPy oracle on sequences {seqs[0]}..{seqs[-1]} ({len(seqs)} of "
+                      f"{case.batch}, {frac:.1%} of query rows, all heads) in {dt:.1f} s, scaled to the "
+                      f"full step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or kv head with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_causal_paged_amd as bcp
+    from workloads import CONFIG_NAMES, config
+    from workloads.device import DeviceCase
+
+    cfg = args.config
+    case = config(cfg)
+    dc = DeviceCase(case)
+    torch.cuda.synchronize()
+    meta = bcp.StepMeta(**dc.meta_kwargs())
+    plan = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda")
+    nqt, nkt = bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
+    tile_class = torch.empty((case.batch, nqt, nkt), dtype=torch.uint8, device="cuda")
+    nct = -(-case.max_kv_len // 64)
+    phys = torch.empty((case.batch, max(nct, 1), max(1, 64 // case.page_size)), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, bcp.attn_workspace_size(meta)), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dc.q)
+    k_cache, v_cache = dc.k_cache, dc.v_cache
+    dst = dc.kv_len
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        bcp.build_tile_mask(meta, tile_class=tile_class, phys_page=phys if nct else None, plan=plan)
+        if evs: evs[1].record()
+        bcp.attn_block_causal_paged(meta, dc.q, dc.k_new, dc.v_new, k_cache, v_cache, out, plan=plan,
+                                    workspace=ws)
+        if evs: evs[2].record()
+        bcp.kv_commit_block(meta, dc.k_new, dc.v_new, dc.cu_q, dst, k_cache, v_cache, case.total_q)
+        if evs: evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Cold steps: flush, then one step bracketed by events.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        flush.fill_(k & 0xFF)
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = np.array([e[0].elapsed_time(e[3]) * 1e3 for e in evs])
+    cls_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    attn_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
+    com_us = np.array([e[2].elapsed_time(e[3]) * 1e3 for e in evs])
+
+    # Warm steps: back to back, no flush.
+    warm_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n_warm = max(args.steps, 20)
+    warm_ev[0].record()
+    for _ in range(n_warm):
+        step()
+    warm_ev[1].record()
+    torch.cuda.synchronize()
+    warm_step_us = warm_ev[0].elapsed_time(warm_ev[1]) * 1e3 / n_warm
+    attn_warm = []
+    for _ in range(n_warm):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        bcp.attn_block_causal_paged(meta, dc.q, dc.k_new, dc.v_new, k_cache, v_cache, out, plan=plan, workspace=ws)
+        e[1].record()
+        attn_warm.append(e)
+    torch.cuda.synchronize()
+    attn_warm_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in attn_warm]))
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+        dst_buf = torch.empty_like(src)
+        for _ in range(5):
+            dst_buf.copy_(src)
+        torch.cuda.synchronize()
+
+    flops, cached_kv, live_kv, q_o = workload_stats(case)
+    algo_bytes = cached_kv + live_kv + q_o
+    a_med = float(np.median(attn_us))
+    a_mean = float(np.mean(attn_us))
+    bound = BOUND[cfg]
+    if bound == "hbm":
+        achieved, peak, unit = algo_bytes / (a_mean * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        peak = MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else FP32_PEAK_TFLOPS
+        achieved, unit = flops / (a_mean * 1e-6) / 1e12, "TFLOP/s"
+    traffic = traffic_from_profile(cfg)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(float(np.mean(step_us)), 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_us)) / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the named workload)",
+        "config": {"workload": f"C{cfg} {CONFIG_NAMES[cfg]}", "batch": case.batch,
+                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+                   "total_q": case.total_q, "kv_len_mean": float(case.kv_len.mean()),
+                   "kv_len_max": int(case.kv_len.max()), "page_size": case.page_size,
+                   "block_size": case.block_size, "mode": case.mode},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_block_causal_paged (attn_bf16_kernel + combine_kernel)",
+                     "algorithmic_bytes": algo_bytes, "useful_flops": flops,
+                     "launch_us_mean": round(a_mean, 3)},
+        "attention_us": {"median": round(a_med, 3), "mean": round(a_mean, 3),
+                         "p10": round(float(np.percentile(attn_us, 10)), 3),
+                         "p90": round(float(np.percentile(attn_us, 90)), 3),
+                         "warm_median": round(attn_warm_us, 3)},
+        "useful_tflops": round(flops / (a_mean * 1e-6) / 1e12, 2),
+        "kv_gbps": round((cached_kv + live_kv) / (a_mean * 1e-6) / 1e9, 1),
+        "hbm_frac": round(algo_bytes / (a_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(flops / (a_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "build_tile_mask_us": round(float(np.mean(cls_us)), 3),
+        "kv_commit_us": round(float(np.mean(com_us)), 3),
+        "kv_commit_gbps": round(2 * live_kv / (float(np.mean(com_us)) * 1e-6) / 1e9, 1),
+        "warm_step_us": round(warm_step_us, 3),
+        "timed_wall_s_incl_flush": round(wall, 4),
+        "device": torch.cuda.get_device_name(0),
+        "cus": torch.cuda.get_device_properties(0).multi_processor_count,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

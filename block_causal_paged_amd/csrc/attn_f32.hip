@@ -1,0 +1,174 @@
+// Block-causal paged attention for float32 inputs, on the vector ALUs.
+//
+// Same definition, plan, tiling and online softmax as the bf16 matrix-core kernel, with
+// every product and sum in float32 (gfx950's fp32 matrix rate equals its vector rate, so
+// the simple formulation costs nothing in peak). One thread owns one packed query row
+// (rho = position * G + head) of the workgroup's 256; key and value tiles are staged in
+// LDS and read by broadcast.
+#include "bcp_internal.h"
+
+namespace bcp {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+constexpr float kLn2 = 0.69314718055994531f;
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) float ks[kTileK][HD];
+  __shared__ __attribute__((aligned(16))) float vs[kTileK][HD];
+  __shared__ int kblk[kTileK];
+  constexpr int V4 = HD / 4;
+  const int tid = threadIdx.x;
+  const int G = a.G;
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
+  const int n_work = a.plan[0] * a.Hkv;
+  const float* qg = (const float*)a.q;
+  const float sl2 = a.scale_log2;
+  if (a.stats && blockIdx.x == 0 && tid == 0)   // skipped tiles of the whole grid, per kv head
+    atomicAdd(&a.stats[2], (unsigned long long)a.Hkv * ((unsigned long long)L.units * a.nkt - a.plan[3]));
+
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int item = w / a.Hkv, g = w - (w / a.Hkv) * a.Hkv;
+    const int* ip = a.plan + L.items + 4 * (int64_t)item;
+    const int u = ip[0], ob = ip[1], oe = ip[2], pslot = ip[3];
+    const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
+    int q0, q_len;
+    live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
+    const int kvl = clampi(a.kv_len[s], 0, a.max_pages * a.page_size);
+    const int i0 = r * a.tile_q;
+    const int* list = a.plan + L.list + (int64_t)u * a.nkt;
+
+    const int rho = tid;
+    const int pos = i0 + rho / G, hh = rho - (rho / G) * G;
+    const bool valid = pos < q_len;
+    const int64_t row = (int64_t)(q0 + pos) * a.Hq + (int64_t)g * G + hh;
+    float qv[HD], ov[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+      qv[d] = valid ? qg[row * HD + d] : 0.f;
+      ov[d] = 0.f;
+    }
+    const int qblk = !valid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[q0 + pos] : pos / a.block_size);
+    float m = -INFINITY, l = 0.f;
+    int n_partial = 0;
+
+    for (int oi = ob; oi < oe; ++oi) {
+      const int e = list[oi];
+      const int vt = e >> 1;
+      const bool partial = e & 1;
+      n_partial += partial;
+      __syncthreads();
+      for (int idx = tid; idx < kTileK * V4; idx += 256) {
+        const int kappa = idx / V4, c = idx - (idx / V4) * V4;
+        const float *kp = nullptr, *vp = nullptr;
+        if (vt < a.nct) {
+          const int j = vt * kTileK + kappa;
+          const int p = j < kvl ? translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages) : -1;
+          if (p >= 0) {
+            const int64_t off = (((int64_t)p * a.page_size + (j % a.page_size)) * a.Hkv + g) * HD;
+            kp = (const float*)a.k_cache + off;
+            vp = (const float*)a.v_cache + off;
+          }
+        } else {
+          const int j = (vt - a.nct) * kTileK + kappa;
+          if (j < q_len) {
+            const int64_t off = ((int64_t)(q0 + j) * a.Hkv + g) * HD;
+            kp = (const float*)a.k_new + off;
+            vp = (const float*)a.v_new + off;
+          }
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)&ks[kappa][4 * c] = kp ? *(const f32x4*)(kp + 4 * c) : z;
+        *(f32x4*)&vs[kappa][4 * c] = vp ? *(const f32x4*)(vp + 4 * c) : z;
+      }
+      if (partial && tid < kTileK) {
+        int b;
+        if (vt < a.nct) {
+          const int j = vt * kTileK + tid;
+          const int p = j < kvl ? translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages) : -1;
+          b = p < 0 ? kNoKeyBlk : (a.mode_b ? a.kv_blk[(int64_t)p * a.page_size + (j % a.page_size)] : kNegInfBlk);
+        } else {
+          const int j = (vt - a.nct) * kTileK + tid;
+          b = j >= q_len ? kNoKeyBlk : (a.mode_b ? a.q_blk[q0 + j] : j / a.block_size);
+        }
+        kblk[tid] = b;
+      }
+      __syncthreads();
+
+      float sc[kTileK];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kTileK; ++k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int d = 0; d < HD; d += 4) {
+          const f32x4 kk = *(const f32x4*)&ks[k][d];
+          acc = fmaf(qv[d], kk[0], acc);
+          acc = fmaf(qv[d + 1], kk[1], acc);
+          acc = fmaf(qv[d + 2], kk[2], acc);
+          acc = fmaf(qv[d + 3], kk[3], acc);
+        }
+        if (partial && kblk[k] > qblk) acc = -INFINITY;
+        sc[k] = acc;
+        mx = fmaxf(mx, acc);
+      }
+      const float mnew = fmaxf(m, mx * sl2);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m - muse);
+      m = mnew;
+      float rs = 0.f;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) ov[d] *= alpha;
+#pragma unroll
+      for (int k = 0; k < kTileK; ++k) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[k], sl2, -muse));
+        rs += p;
+#pragma unroll
+        for (int d = 0; d < HD; d += 4) {
+          const f32x4 vv = *(const f32x4*)&vs[k][d];
+          ov[d] = fmaf(p, vv[0], ov[d]);
+          ov[d + 1] = fmaf(p, vv[1], ov[d + 1]);
+          ov[d + 2] = fmaf(p, vv[2], ov[d + 2]);
+          ov[d + 3] = fmaf(p, vv[3], ov[d + 3]);
+        }
+      }
+      l = l * alpha + rs;
+    }
+
+    if (valid) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float lse2 = l > 0.f ? m + __log2f(l) : -INFINITY;
+      if (pslot < 0) {
+        float* op = (float*)a.out + row * HD;
+#pragma unroll
+        for (int d = 0; d < HD; d += 4) *(f32x4*)(op + d) = f32x4{ov[d] * inv, ov[d + 1] * inv, ov[d + 2] * inv, ov[d + 3] * inv};
+        if (a.lse) a.lse[row] = lse2 * kLn2;
+      } else {
+        const int64_t slot = (int64_t)pslot * a.Hkv + g;
+        float* pp = a.part_o + (slot * kRowsPerWG + rho) * HD;
+#pragma unroll
+        for (int d = 0; d < HD; d += 4) *(f32x4*)(pp + d) = f32x4{ov[d] * inv, ov[d + 1] * inv, ov[d + 2] * inv, ov[d + 3] * inv};
+        a.part_lse[slot * kRowsPerWG + rho] = lse2;
+      }
+    }
+    if (a.stats && tid == 0) {
+      const int n = oe - ob;
+      atomicAdd(&a.stats[0], (unsigned long long)(n - n_partial));
+      atomicAdd(&a.stats[1], (unsigned long long)n_partial);
+      atomicAdd(&a.stats[3], (unsigned long long)n * 2ull * kTileK * HD * 4ull);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bcp

@@ -1,0 +1,148 @@
+// Internal definitions shared by the host ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bcp.h"
+
+namespace bcp {
+
+// Attention tiling. One workgroup owns 256 packed query rows: tile_q consecutive live
+// positions of one sequence times the G = Hq/Hkv query heads that share one kv head,
+// packed position-major (row rho = position * G + head-in-group). Keys stream in tiles of
+// kTileK rows.
+constexpr int kTileK = 64;
+constexpr int kRowsPerWG = 256;
+
+// Split-KV planning. A unit is one (sequence, q-tile); its non-skipped key tiles are cut
+// into nearly equal chunks so that the step has about kTargetWGs (chunk, kv head) work
+// items in total, each at least kMinChunk tiles long. Proof of the bounds used for buffer
+// sizes: with c = max(kMinChunk, ceil(T*Hkv/kTargetWGs)) and T the non-skipped tile total,
+// sum_u ceil(cnt_u/c) <= T/c + U <= kTargetWGs/Hkv + U items; a split unit has cnt_u > c,
+// so its ceil(cnt_u/c) < 2*cnt_u/c and all split items times Hkv stay below 2*kTargetWGs.
+constexpr int kTargetWGs = 512;
+constexpr int kMinChunk = 4;
+constexpr int kMaxPartialSlots = 2 * kTargetWGs;
+
+constexpr int kNegInfBlk = INT32_MIN;   // a committed row in mode A: seen by every live row
+constexpr int kNoKeyBlk = INT32_MAX;    // an absent key: seen by nobody
+
+// Step plan, in int32 words:
+//   [0, 8)                header: n_items, n_split_units, chunk, total tiles, tile_q, tile_k,
+//                         nqt, nkt
+//   cnt   [U]             non-skipped key tiles per unit (U = batch * nqt)
+//   list  [U * nkt]       per unit, its non-skipped virtual tile indices in order, each
+//                         stored as (t << 1) | is_partial; t < nct is cached tile t,
+//                         t >= nct is live tile t - nct
+//   items [max_items][4]  unit, first ordinal, end ordinal, partial slot (-1: unit not split)
+//   split [U][4]          unit, first partial slot, number of splits, 0
+struct PlanLayout {
+  int64_t cnt, list, items, split, words;
+  int units, nkt, max_items;
+};
+
+__host__ __device__ inline PlanLayout plan_layout(int batch, int nqt, int nkt) {
+  PlanLayout p;
+  p.units = batch * nqt;
+  p.nkt = nkt;
+  p.max_items = p.units + kTargetWGs;
+  p.cnt = 8;
+  p.list = p.cnt + p.units;
+  p.items = p.list + (int64_t)p.units * nkt;
+  p.split = p.items + 4 * (int64_t)p.max_items;
+  p.words = p.split + 4 * (int64_t)p.units;
+  return p;
+}
+
+struct ClassifyArgs {
+  const int32_t* cu_q;
+  const int32_t* kv_len;
+  const int32_t* page_table;
+  const int32_t* q_blk;
+  const int32_t* kv_blk;
+  uint8_t* tile_class;    // may be null
+  int32_t* phys_page;     // may be null
+  int32_t* plan;          // may be null
+  int batch, total_q, tile_q, tile_k, nqt, nct, nkt, block_size, page_size, num_pages,
+      max_pages, max_q_len, mode_b, phys_per_tile, phys_tiles;
+  int grid_q;             // q-tile workgroups per sequence: max(nqt, 1)
+};
+
+struct PlanArgs {
+  int32_t* plan;
+  int batch, nqt, nkt, num_kv_heads, tile_q, tile_k;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* k_cache;
+  const void* v_cache;
+  void* out;
+  float* lse;
+  float* part_o;          // [kMaxPartialSlots][256][d] normalized partial outputs
+  float* part_lse;        // [kMaxPartialSlots][256] log2-domain partial LSE
+  const int32_t* cu_q;
+  const int32_t* kv_len;
+  const int32_t* page_table;
+  const int32_t* q_blk;
+  const int32_t* kv_blk;
+  const int32_t* plan;
+  unsigned long long* stats;
+  int batch, total_q, max_q_len, Hq, Hkv, G, tile_q, nqt, nkt, nct, page_size, num_pages,
+      max_pages, block_size, mode_b, max_items;
+  float scale_log2;       // softmax scale times log2(e)
+};
+
+struct CommitArgs {
+  const void* k_src;
+  const void* v_src;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* cu_src;
+  const int32_t* src_row;
+  const int32_t* dst_start;
+  const int32_t* src_blk;
+  int32_t* kv_blk_out;
+  const int32_t* page_table;
+  int batch, total, n_src, row_chunks, page_size, num_pages, max_pages;
+};
+
+hipError_t launch_classify(const ClassifyArgs& a, hipStream_t stream);
+hipError_t launch_planner(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_combine(const AttnArgs& a, int head_dim, int is_bf16, int grid,
+                          hipStream_t stream);
+hipError_t launch_commit(const CommitArgs& a, int grid, hipStream_t stream);
+
+// ----------------------------------------------------------------------------------------
+// Device helpers shared by the kernels.
+// ----------------------------------------------------------------------------------------
+#ifdef __HIPCC__
+// Page translation: physical page of logical row j of sequence s, or -1 when the row lies
+// beyond max_pages_per_seq pages or its page id is outside the pool ("Paged Attention":
+// the page table maps logical rows onto physical pages).
+__device__ __forceinline__ int translate_page(const int32_t* __restrict__ page_table, int s, int j,
+                                              int page_size, int max_pages, int num_pages) {
+  if (j < 0) return -1;
+  int lp = j / page_size;
+  if (lp >= max_pages) return -1;
+  int p = page_table[(int64_t)s * max_pages + lp];
+  return (p >= 0 && p < num_pages) ? p : -1;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Live rows of sequence s, clamped so that [*q0, *q0 + *q_len) lies inside [0, total_q).
+__device__ __forceinline__ void live_rows(const int32_t* __restrict__ cu_q, int s, int total_q,
+                                          int max_q_len, int* q0, int* q_len) {
+  const int a = clampi(cu_q[s], 0, total_q);
+  *q0 = a;
+  *q_len = clampi(cu_q[s + 1] - a, 0, min(max_q_len, total_q - a));
+}
+#endif
+
+}  // namespace bcp

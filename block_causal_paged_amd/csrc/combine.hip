@@ -1,0 +1,75 @@
+// Merge of split-KV partial results.
+//
+// A q-tile whose key tiles were cut into several chunks has one partial result per chunk:
+// the chunk's softmax-normalized output O_c and its log-sum-exp lse_c (log2 domain). The
+// softmax over the union of the chunks is their lse-weighted mean:
+//   M = max_c lse_c,  w_c = 2^(lse_c - M),  O = sum_c w_c O_c / sum_c w_c,
+//   lse = M + log2(sum_c w_c).
+// This is the same online-softmax identity the attention kernel applies tile by tile.
+#include "bcp_internal.h"
+
+namespace bcp {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+constexpr float kLn2 = 0.69314718055994531f;
+
+template <int HD, bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  constexpr int V4 = HD / 4;              // float4 per row
+  constexpr int RPP = 256 / V4;           // rows per pass of the workgroup
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
+  const int n_work = a.plan[1] * a.Hkv;
+  const int tid = threadIdx.x, d4 = tid % V4;
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int e = w / a.Hkv, g = w - (w / a.Hkv) * a.Hkv;
+    const int* sp = a.plan + L.split + 4 * (int64_t)e;
+    const int u = sp[0], ps0 = sp[1], n = sp[2];
+    const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
+    int q0, q_len;
+    live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
+    const int i0 = r * a.tile_q;
+    for (int rho = tid / V4; rho < kRowsPerWG; rho += RPP) {
+      const int pos = i0 + rho / a.G, hh = rho - (rho / a.G) * a.G;
+      if (pos >= q_len) continue;
+      float M = -INFINITY;
+      for (int c = 0; c < n; ++c)
+        M = fmaxf(M, a.part_lse[((int64_t)(ps0 + c) * a.Hkv + g) * kRowsPerWG + rho]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      float wsum = 0.f;
+      if (M != -INFINITY) {
+        for (int c = 0; c < n; ++c) {
+          const int64_t slot = (int64_t)(ps0 + c) * a.Hkv + g;
+          const float wc = __builtin_amdgcn_exp2f(a.part_lse[slot * kRowsPerWG + rho] - M);
+          const f32x4 oc = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+          acc += wc * oc;
+          wsum += wc;
+        }
+        acc *= 1.f / wsum;
+      }
+      const int64_t row = (int64_t)(q0 + pos) * a.Hq + (int64_t)g * a.G + hh;
+      if constexpr (BF16_OUT) {
+        *(bf16x4*)((uint16_t*)a.out + row * HD + 4 * d4) = __builtin_convertvector(acc, bf16x4);
+      } else {
+        *(f32x4*)((float*)a.out + row * HD + 4 * d4) = acc;
+      }
+      if (d4 == 0 && a.lse) a.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(wsum)) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const AttnArgs& a, int head_dim, int is_bf16, int grid, hipStream_t stream) {
+  if (head_dim == 128) {
+    if (is_bf16) hipLaunchKernelGGL((combine_kernel<128, true>), dim3(grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<128, false>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((combine_kernel<64, true>), dim3(grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<64, false>), dim3(grid), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bcp

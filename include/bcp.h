@@ -1,0 +1,196 @@
+/*
+ * bcp.h -- block-causal paged attention and KV commit for MI355X (gfx950).
+ *
+ * The operation (from "Inference for Interpretable Text-Diffusion Models", Background
+ * and sections "FlexAttention with Aligned Tiles", "KV Cache", "Paged Attention"; and
+ * "Inference: Fewer, smaller forwards", Advancements 1, 11 and 13):
+ *
+ *   A batch of sequences each has kv_len committed rows whose keys/values sit in a
+ *   paged cache (fixed-size pages anywhere in a pool, located through a page table),
+ *   and q_len live rows of the active block(s), whose queries, keys and values are
+ *   passed in. Every live row attends
+ *     mode A: to all committed rows, and to live row j iff j/D <= i/D (blocks of D rows
+ *             counted from the sequence's first live row: bidirectional inside a block,
+ *             causal across blocks, never to later blocks);
+ *     mode B: to committed row j iff kv_blk[slot(j)] <= q_blk[i], and to live row j iff
+ *             q_blk[j] <= q_blk[i] (block ids per row, as in multi-canvas decoding where
+ *             canvas c sees the prompt, earlier canvases and itself).
+ *   out = softmax(scale * q k^T restricted to visible keys) v, per query head, with
+ *   grouped-query attention: query head h reads kv head h / (Hq / Hkv).
+ *   When a block is finished its rows are committed: copied bit for bit into the page
+ *   slots that follow the sequence's committed rows.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer unless marked (host). All buffers are owned by
+ *     the caller; the library allocates no device memory, keeps no pointer past a call
+ *     and has no global state other than a thread-local error message and a per-device
+ *     cache of the compute-unit count.
+ *   - Work is enqueued asynchronously on `stream`; no entry point synchronizes, except
+ *     in checked mode (BCP_F_CHECK), which copies the metadata to the host once and
+ *     validates it before launching anything.
+ *   - Host-visible arguments are always validated before any launch. On a non-OK
+ *     return nothing has been enqueued and no output was touched; bcp_last_error()
+ *     describes the failure.
+ *   - Device-side content (lengths, page ids, block ids, row indices) is validated only
+ *     in checked mode. Without it, bad content gives unspecified results, but every
+ *     kernel bounds-checks page ids and row indices, so it never reads or writes
+ *     outside the buffers described here.
+ *   - Tensors are dense, row-major, 16-byte aligned.
+ */
+#ifndef BCP_H
+#define BCP_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BCP_ABI_VERSION 1
+
+enum { BCP_BF16 = 0, BCP_F32 = 1 };
+enum { BCP_TILE_SKIP = 0, BCP_TILE_PARTIAL = 1, BCP_TILE_FULL = 2 };
+enum {
+  BCP_OK = 0,
+  BCP_E_ARG = 1,          /* malformed host argument (null, size, alignment, tile size) */
+  BCP_E_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, dtype, group size) */
+  BCP_E_RANGE = 3,        /* checked mode: device metadata out of range or duplicated */
+  BCP_E_WORKSPACE = 4,    /* workspace or plan buffer too small */
+  BCP_E_HIP = 5           /* a HIP runtime call failed */
+};
+#define BCP_F_CHECK 1u    /* validate device metadata before launch (one device->host sync) */
+
+/*
+ * Geometry of one step, shared by every call of the step (and every layer).
+ * Layouts:
+ *   q       [total_q, Hq, d]            live queries of the active blocks
+ *   k_new   [total_q, Hkv, d]           live keys (positional encoding already applied)
+ *   v_new   [total_q, Hkv, d]
+ *   cache   [num_pages, page_size, Hkv, d]  one pool each for K and V (one layer)
+ * Logical committed row j of sequence s lives in page page_table[s*max_pages_per_seq +
+ * j/page_size], slot j%page_size ("Paged Attention": the page table maps the logical
+ * layout onto physical pages).
+ */
+typedef struct bcp_meta {
+  uint32_t struct_size;        /* sizeof(bcp_meta) */
+  int32_t dtype;               /* BCP_BF16 or BCP_F32, for q, k/v (live and cache) and out */
+  int32_t batch;               /* number of sequences, >= 1 */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0 and 256 % (Hq/Hkv) == 0 */
+  int32_t head_dim;            /* d: 64 or 128 */
+  int32_t block_size;          /* D >= 1: live rows per block (mode A) */
+  const int32_t* cu_q;         /* [batch+1] live-row offsets; cu_q[0] = 0, cu_q[batch] = total_q */
+  const int32_t* q_blk;        /* [total_q] block id per live row, or NULL (mode A) */
+  int32_t total_q;             /* host copy of cu_q[batch] */
+  int32_t max_q_len;           /* host bound on cu_q[s+1]-cu_q[s] */
+  const int32_t* kv_len;       /* [batch] committed rows per sequence */
+  const int32_t* page_table;   /* [batch, max_pages_per_seq] physical page ids */
+  const int32_t* kv_blk;       /* [num_pages*page_size] block id per cache slot, or NULL (mode A) */
+  int32_t num_pages;           /* pool size in pages */
+  int32_t page_size;           /* P >= 1 */
+  int32_t max_pages_per_seq;   /* row stride of page_table */
+  int32_t max_kv_len;          /* host bound on kv_len[s] */
+  int32_t tile_q;              /* query positions per q-tile; 0 -> 256/(Hq/Hkv) */
+  int32_t tile_k;              /* keys per k-tile; 0 -> 64 */
+  uint32_t flags;              /* BCP_F_CHECK */
+} bcp_meta;
+
+/* Number of query tiles / key tiles of the step's tile grid (after the tile defaults).
+ * nqt = ceil(max_q_len/tile_q); nkt = ceil(max_kv_len/tile_k) + ceil(max_q_len/tile_k):
+ * the cached key tiles come first, then the live key tiles. Returns 0 on a bad meta. */
+int32_t bcp_num_q_tiles(const bcp_meta* m);
+int32_t bcp_num_k_tiles(const bcp_meta* m);
+
+/* Device bytes of the step plan that build_tile_mask writes and attn_block_causal_paged
+ * reads (0 on a bad meta). */
+size_t bcp_plan_size(const bcp_meta* m);
+
+/*
+ * build_tile_mask -- classify every (query tile, key tile) pair of every sequence
+ * ("FlexAttention with Aligned Tiles": a tile is fully included, fully excluded or
+ * partially included; included tiles need no masking, excluded tiles no work).
+ * A tile is SKIP if no in-range row sees any of its columns, FULL if every in-range row
+ * sees all tile_k columns (a column past its region's length counts as not visible), and
+ * PARTIAL otherwise. Computed from block-id ranges: SKIP iff (no valid row or column) or
+ * min key block > max query block; FULL iff max key block <= min query block and all
+ * tile_k columns are valid. Committed rows in mode A count as block -infinity.
+ *
+ *   tile_class  [batch, nqt, nkt] uint8 BCP_TILE_* codes, or NULL.
+ *   phys_page   [batch, ceil(max_kv_len/tile_k), max(1, tile_k/page_size)] int32, or NULL:
+ *               the physical page holding row t*tile_k + u*page_size of sequence s (the page
+ *               table applied to the tile grid), -1 at or past kv_len[s]. When
+ *               page_size > tile_k there is one entry per tile: the page of its first row.
+ *   plan        [bcp_plan_size(m) bytes], or NULL: the step plan for attn_block_causal_paged
+ *               (per q-tile list of non-skipped key tiles and a balanced split-KV work
+ *               list). Only valid for the attention tile sizes (tile_q = 256/(Hq/Hkv),
+ *               tile_k = 64) and only for metadata identical to the attention call's.
+ * At least one output must be non-NULL. Errors: BCP_E_ARG, BCP_E_WORKSPACE (plan_bytes too
+ * small), BCP_E_RANGE (checked mode), BCP_E_HIP.
+ */
+int build_tile_mask(const bcp_meta* m, uint8_t* tile_class, int32_t* phys_page, void* plan,
+                    size_t plan_bytes, hipStream_t stream);
+
+/* Device workspace bytes attn_block_causal_paged needs: the split-KV partial results, and
+ * room to build the plan itself when it is called with plan == NULL. */
+size_t attn_block_causal_paged_workspace_size(const bcp_meta* m);
+
+/*
+ * attn_block_causal_paged -- block-causal attention of the live rows over the paged cache
+ * and the live rows themselves (definition at the top of this file).
+ *   q, k_new, v_new, k_cache, v_cache: layouts above, dtype m->dtype.
+ *   plan        from build_tile_mask with the same meta, or NULL (then it is built in the
+ *               workspace first, costing two extra kernel launches).
+ *   scale       softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   out         [total_q, Hq, d] dtype m->dtype (bf16 rounded to nearest even).
+ *   lse         [total_q, Hq] float32 natural-log sum of exp of the scaled visible scores,
+ *               or NULL.
+ *   workspace   >= attn_block_causal_paged_workspace_size(m) bytes (need not be zeroed).
+ *   stats       uint64[4] or NULL: counters incremented by this call -- FULL tiles
+ *               computed, PARTIAL tiles computed, SKIP tiles not loaded (each per kv head),
+ *               K/V bytes loaded.
+ * Supported: head_dim 64/128; bf16 (MFMA path) or f32 (vector path); tile_q and tile_k
+ * must equal their defaults. Every row must see at least one key (always true: a live row
+ * sees itself); a row that sees none gets out = 0 and lse = -inf.
+ * Errors: BCP_E_ARG, BCP_E_UNSUPPORTED, BCP_E_WORKSPACE, BCP_E_RANGE (checked), BCP_E_HIP.
+ */
+int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
+                            const void* v_new, const void* k_cache, const void* v_cache,
+                            const void* plan, float scale, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, uint64_t* stats,
+                            hipStream_t stream);
+
+/*
+ * kv_commit_block -- write finished rows into their cache pages ("KV Cache", step 3: after
+ * a block is fully unmasked its keys and values are committed; "Fewer, smaller forwards",
+ * Advancement 11: arena entries carry their position tag, here the block id).
+ * For sequence s and r < cu_src[s+1]-cu_src[s]: source row
+ *   row = src_row ? src_row[cu_src[s]+r] : cu_src[s]+r
+ * is copied bit for bit from k_src/v_src [n_src, Hkv, d] to logical row dst_start[s]+r of
+ * sequence s, i.e. page page_table[s, (dst_start[s]+r)/P], slot (dst_start[s]+r)%P, of
+ * k_cache/v_cache; kv_blk_out[page*P+slot] = src_blk[row] when both are non-NULL. Every
+ * other byte of the caches is left as it was. The caller maps the pages beforehand and
+ * advances kv_len afterwards; the library never changes metadata.
+ *   cu_src [batch+1], src_row [total_commit] or NULL, dst_start [batch],
+ *   src_blk [n_src] or NULL, kv_blk_out [num_pages*P] or NULL.
+ *   total_commit = host copy of cu_src[batch]; n_src = rows in k_src/v_src.
+ * Two rows with the same destination slot race (checked mode rejects it with BCP_E_RANGE).
+ * Uses m's dtype, batch, Hkv, head_dim, page_table, num_pages, page_size,
+ * max_pages_per_seq and flags.
+ */
+int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src,
+                    const int32_t* cu_src, const int32_t* src_row, const int32_t* dst_start,
+                    const int32_t* src_blk, int32_t total_commit, int32_t n_src,
+                    void* k_cache, void* v_cache, int32_t* kv_blk_out, hipStream_t stream);
+
+/* Thread-local description of the last non-OK return on this thread (host string). */
+const char* bcp_last_error(void);
+
+/* BCP_ABI_VERSION of the loaded library. */
+int bcp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BCP_H */

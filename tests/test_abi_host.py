@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI, runnable without a GPU.
+
+The library must load and export every function include/bcp.h declares, and every
+malformed host argument must be rejected with its status code before anything touches a
+device (the pointers used here are fake, never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_causal_paged_amd as bcp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "bcp.h")
+FAKE = 0x10000   # a 64 KiB-aligned fake device address; validation only checks alignment
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    L = bcp.lib()
+    decl = declared_functions()
+    assert set(decl) == set(bcp.EXPORTED), decl
+    for name in decl:
+        assert hasattr(L, name), name
+    assert L.bcp_abi_version() == 1
+
+
+def meta(**over):
+    kw = dict(struct_size=ctypes.sizeof(bcp.bcp_meta), dtype=bcp.BCP_BF16, batch=8, num_q_heads=32,
+              num_kv_heads=8, head_dim=128, block_size=64, cu_q=FAKE, q_blk=None, total_q=512,
+              max_q_len=64, kv_len=FAKE, page_table=FAKE, kv_blk=None, num_pages=4096, page_size=64,
+              max_pages_per_seq=65, max_kv_len=4096, tile_q=0, tile_k=0, flags=0)
+    kw.update(over)
+    return bcp.bcp_meta(**kw)
+
+
+def attn(m, workspace_bytes=1 << 40, **over):
+    args = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, plan=FAKE, scale=0.0,
+                out=FAKE, lse=None, ws=FAKE, wsb=workspace_bytes, stats=None)
+    args.update(over)
+    return bcp.lib().attn_block_causal_paged(ctypes.byref(m), args["q"], args["k_new"], args["v_new"],
+                                             args["k_cache"], args["v_cache"], args["plan"],
+                                             args["scale"], args["out"], args["lse"], args["ws"],
+                                             args["wsb"], args["stats"], None)
+
+
+def test_geometry_queries():
+    m = meta()
+    L = bcp.lib()
+    assert L.bcp_num_q_tiles(ctypes.byref(m)) == 1          # 64 positions x 4 heads = 256 rows
+    assert L.bcp_num_k_tiles(ctypes.byref(m)) == 64 + 1     # 4096/64 cached + 1 live
+    assert L.bcp_plan_size(ctypes.byref(m)) > 0
+    assert L.attn_block_causal_paged_workspace_size(ctypes.byref(m)) > 0
+    assert L.bcp_plan_size(ctypes.byref(meta(struct_size=4))) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(struct_size=8), bcp.BCP_E_ARG),
+    (dict(dtype=7), bcp.BCP_E_ARG),
+    (dict(batch=0), bcp.BCP_E_ARG),
+    (dict(num_q_heads=30), bcp.BCP_E_ARG),                # not a multiple of 8 kv heads
+    (dict(cu_q=None), bcp.BCP_E_ARG),
+    (dict(kv_len=FAKE + 2), bcp.BCP_E_ARG),               # misaligned metadata
+    (dict(q_blk=FAKE), bcp.BCP_E_ARG),                    # mode B needs both id arrays
+    (dict(block_size=0), bcp.BCP_E_ARG),
+    (dict(page_size=0), bcp.BCP_E_ARG),
+    (dict(total_q=513), bcp.BCP_E_ARG),                   # more than batch * max_q_len
+    (dict(max_kv_len=65 * 64 + 1), bcp.BCP_E_ARG),        # beyond the page table's reach
+    (dict(head_dim=96), bcp.BCP_E_UNSUPPORTED),
+    (dict(num_q_heads=24), bcp.BCP_E_UNSUPPORTED),        # 3 query heads per kv head
+    (dict(tile_q=32), bcp.BCP_E_UNSUPPORTED),
+    (dict(tile_k=32), bcp.BCP_E_UNSUPPORTED),
+])
+def test_attention_rejects_bad_meta(over, code):
+    assert attn(meta(**over)) == code
+    assert bcp.lib().bcp_last_error()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), bcp.BCP_E_ARG),
+    (dict(out=FAKE + 8), bcp.BCP_E_ARG),                  # misaligned tensor
+    (dict(scale=float("nan")), bcp.BCP_E_ARG),
+    (dict(wsb=16), bcp.BCP_E_WORKSPACE),
+    (dict(plan=None, wsb=1024), bcp.BCP_E_WORKSPACE),     # building the plan needs room too
+])
+def test_attention_rejects_bad_buffers(over, code):
+    assert attn(meta(), **over) == code
+
+
+def test_tile_mask_rejects():
+    L = bcp.lib()
+    m = meta()
+    assert L.build_tile_mask(ctypes.byref(m), None, None, None, 0, None) == bcp.BCP_E_ARG
+    assert L.build_tile_mask(ctypes.byref(m), None, None, FAKE, 64, None) == bcp.BCP_E_WORKSPACE
+    assert L.build_tile_mask(ctypes.byref(meta(struct_size=1)), FAKE, None, None, 0, None) == bcp.BCP_E_ARG
+    assert b"NULL" in L.bcp_last_error() or L.bcp_last_error()
+
+
+def test_commit_rejects():
+    L = bcp.lib()
+
+    def commit(m, **over):
+        a = dict(k_src=FAKE, v_src=FAKE, cu_src=FAKE, src_row=None, dst_start=FAKE, src_blk=None,
+                 total=4, n_src=4, k_cache=FAKE, v_cache=FAKE, kv_blk_out=None)
+        a.update(over)
+        return L.kv_commit_block(ctypes.byref(m), a["k_src"], a["v_src"], a["cu_src"], a["src_row"],
+                                 a["dst_start"], a["src_blk"], a["total"], a["n_src"], a["k_cache"],
+                                 a["v_cache"], a["kv_blk_out"], None)
+
+    assert commit(meta(struct_size=3)) == bcp.BCP_E_ARG
+    assert commit(meta(), k_cache=None) == bcp.BCP_E_ARG
+    assert commit(meta(), total=-1) == bcp.BCP_E_ARG
+    assert commit(meta(), v_src=FAKE + 4) == bcp.BCP_E_ARG
+    assert commit(meta(head_dim=4, num_kv_heads=1)) == bcp.BCP_E_UNSUPPORTED   # 8-byte rows
+    assert commit(meta(), total=0) == bcp.BCP_OK                              # nothing to do
+
+
+def test_error_message_is_thread_local_and_specific():
+    attn(meta(head_dim=96))
+    assert b"head_dim 96" in bcp.lib().bcp_last_error()

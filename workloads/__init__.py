@@ -67,6 +67,9 @@ class Case:
     q_blk: Optional[np.ndarray] = None
     kv_blk: Optional[np.ndarray] = None
     desc: str = ""
+    # Mode B structure in logical row order, per sequence (what the page placement used).
+    q_blk_seqs: Optional[list] = None
+    kv_blk_seqs: Optional[list] = None
 
     @property
     def total_q(self) -> int:
@@ -207,6 +210,8 @@ def make_case(
         block_size=int(block_size), page_size=P, num_pages=int(num_pages), cu_q=cu_q,
         kv_len=kv_lens.astype(np.int32), page_table=page_table, q=q, k_new=k_new, v_new=v_new,
         k_cache=k_cache, v_cache=v_cache, q_blk=q_blk, kv_blk=kv_blk, desc=desc,
+        q_blk_seqs=None if q_blk is None else [np.asarray(b, np.int32) for b in q_blk_seqs],
+        kv_blk_seqs=None if q_blk is None else [np.asarray(b, np.int32) for b in kv_blk_seqs],
     )
 
 
