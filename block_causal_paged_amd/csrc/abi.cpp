@@ -339,6 +339,7 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   a.block_size = g.mode_b ? 1 : m->block_size;
   a.mode_b = g.mode_b;
   a.max_items = plan_layout(m->batch, g.nqt, g.nkt).max_items;
+  a.page_shift = (m->page_size & (m->page_size - 1)) ? -1 : __builtin_ctz((unsigned)m->page_size);
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)m->head_dim);
   a.scale_log2 = sc * 1.4426950408889634f;
 
@@ -349,7 +350,7 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
                                       : launch_attn_f32(a, m->head_dim, grid, stream);
   if (e != hipSuccess) return hip_fail(e, "launch attention");
   if (part) {
-    const int cgrid = (int)std::min<int64_t>(kMaxPartialSlots, (int64_t)cus * 4);
+    const int cgrid = (int)std::min<int64_t>((int64_t)kMaxPartialSlots * 16, (int64_t)cus * 8);
     e = launch_combine(a, m->head_dim, m->dtype == BCP_BF16, cgrid, stream);
     if (e != hipSuccess) return hip_fail(e, "launch combine");
   }

@@ -21,7 +21,7 @@ constexpr int kRowsPerWG = 256;
 // sizes: with c = max(kMinChunk, ceil(T*Hkv/kTargetWGs)) and T the non-skipped tile total,
 // sum_u ceil(cnt_u/c) <= T/c + U <= kTargetWGs/Hkv + U items; a split unit has cnt_u > c,
 // so its ceil(cnt_u/c) < 2*cnt_u/c and all split items times Hkv stay below 2*kTargetWGs.
-constexpr int kTargetWGs = 512;
+constexpr int kTargetWGs = 256;
 constexpr int kMinChunk = 4;
 constexpr int kMaxPartialSlots = 2 * kTargetWGs;
 
@@ -93,6 +93,7 @@ struct AttnArgs {
   unsigned long long* stats;
   int batch, total_q, max_q_len, Hq, Hkv, G, tile_q, nqt, nkt, nct, page_size, num_pages,
       max_pages, block_size, mode_b, max_items;
+  int page_shift;         // log2(page_size) when it is a power of two, else -1
   float scale_log2;       // softmax scale times log2(e)
 };
 
@@ -133,6 +134,21 @@ __device__ __forceinline__ int translate_page(const int32_t* __restrict__ page_t
   int p = page_table[(int64_t)s * max_pages + lp];
   return (p >= 0 && p < num_pages) ? p : -1;
 }
+
+// Row j's logical page and slot, with shifts when the page size is a power of two.
+__device__ __forceinline__ void page_split(int j, int page_size, int page_shift, int* lp, int* slot) {
+  if (page_shift >= 0) {
+    *lp = j >> page_shift;
+    *slot = j & (page_size - 1);
+  } else {
+    *lp = j / page_size;
+    *slot = j - *lp * page_size;
+  }
+}
+
+// Read-only device data through the scalar cache when the address is uniform.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ cint32* as_const(const int32_t* p) { return (cint32*)p; }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 

@@ -18,44 +18,58 @@ constexpr float kLn2 = 0.69314718055994531f;
 template <int HD, bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   constexpr int V4 = HD / 4;              // float4 per row
-  constexpr int RPP = 256 / V4;           // rows per pass of the workgroup
+  constexpr int RPW = 256 / V4;           // rows per work item (one row per V4 threads)
+  constexpr int NGRP = kRowsPerWG / RPW;  // row groups per (split unit, kv head)
+  constexpr int MAXC = 8;                 // splits merged per pass, loads issued together
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
-  const int n_work = a.plan[1] * a.Hkv;
-  const int tid = threadIdx.x, d4 = tid % V4;
+  cint32* plan = as_const(a.plan);
+  const int n_work = plan[1] * a.Hkv * NGRP;
+  const int tid = threadIdx.x, d4 = tid % V4, rr = tid / V4;
   for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int e = w / a.Hkv, g = w - (w / a.Hkv) * a.Hkv;
-    const int* sp = a.plan + L.split + 4 * (int64_t)e;
+    const int grp = w % NGRP, eg = w / NGRP;
+    const int e = eg / a.Hkv, g = eg - (eg / a.Hkv) * a.Hkv;
+    cint32* sp = plan + L.split + 4 * (int64_t)e;
     const int u = sp[0], ps0 = sp[1], n = sp[2];
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
     int q0, q_len;
     live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
-    const int i0 = r * a.tile_q;
-    for (int rho = tid / V4; rho < kRowsPerWG; rho += RPP) {
-      const int pos = i0 + rho / a.G, hh = rho - (rho / a.G) * a.G;
-      if (pos >= q_len) continue;
-      float M = -INFINITY;
-      for (int c = 0; c < n; ++c)
-        M = fmaxf(M, a.part_lse[((int64_t)(ps0 + c) * a.Hkv + g) * kRowsPerWG + rho]);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      float wsum = 0.f;
-      if (M != -INFINITY) {
-        for (int c = 0; c < n; ++c) {
+    const int rho = grp * RPW + rr;
+    const int pos = r * a.tile_q + rho / a.G, hh = rho - (rho / a.G) * a.G;
+    if (pos >= q_len) continue;
+    // Pass 1: the largest partial LSE. Pass 2: the weighted sum, MAXC splits at a time with
+    // all their loads in flight together.
+    float M = -INFINITY;
+    for (int c = 0; c < n; ++c)
+      M = fmaxf(M, a.part_lse[((int64_t)(ps0 + c) * a.Hkv + g) * kRowsPerWG + rho]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+      for (int c0 = 0; c0 < n; c0 += MAXC) {
+        float lc[MAXC];
+        f32x4 oc[MAXC];
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) {
+          const int c = min(c0 + k, n - 1);
           const int64_t slot = (int64_t)(ps0 + c) * a.Hkv + g;
-          const float wc = __builtin_amdgcn_exp2f(a.part_lse[slot * kRowsPerWG + rho] - M);
-          const f32x4 oc = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
-          acc += wc * oc;
+          lc[k] = a.part_lse[slot * kRowsPerWG + rho];
+          oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+        }
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) {
+          const float wc = c0 + k < n ? __builtin_amdgcn_exp2f(lc[k] - M) : 0.f;
+          acc += wc * oc[k];
           wsum += wc;
         }
-        acc *= 1.f / wsum;
       }
-      const int64_t row = (int64_t)(q0 + pos) * a.Hq + (int64_t)g * a.G + hh;
-      if constexpr (BF16_OUT) {
-        *(bf16x4*)((uint16_t*)a.out + row * HD + 4 * d4) = __builtin_convertvector(acc, bf16x4);
-      } else {
-        *(f32x4*)((float*)a.out + row * HD + 4 * d4) = acc;
-      }
-      if (d4 == 0 && a.lse) a.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(wsum)) * kLn2;
+      acc *= 1.f / wsum;
     }
+    const int64_t row = (int64_t)(q0 + pos) * a.Hq + (int64_t)g * a.G + hh;
+    if constexpr (BF16_OUT) {
+      *(bf16x4*)((uint16_t*)a.out + row * HD + 4 * d4) = __builtin_convertvector(acc, bf16x4);
+    } else {
+      *(f32x4*)((float*)a.out + row * HD + 4 * d4) = acc;
+    }
+    if (d4 == 0 && a.lse) a.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(wsum)) * kLn2;
   }
 }
 
