@@ -95,6 +95,9 @@ SMALL = [
     dict(seed=11, dtype="f32", G=4, d=64, D=1, P=16, mode="B"),
     dict(seed=12, dtype="bf16", G=16, d=128, D=64, P=16, max_q=40, max_kv=2000),
     dict(seed=13, dtype="bf16", G=4, d=128, D=64, P=64, batch=5, max_q=300, max_kv=700),
+    dict(seed=14, dtype="bf16", G=4, d=64, D=1, P=12, mode="B"),
+    dict(seed=15, dtype="bf16", G=8, d=128, D=1, P=3, mode="B", max_kv=500),
+    dict(seed=16, dtype="bf16", G=4, d=128, D=1, P=8, mode="B", max_q=200, max_kv=900),
 ]
 
 
