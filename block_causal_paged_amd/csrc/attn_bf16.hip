@@ -55,11 +55,15 @@ constexpr int kRowsPerWave = kTileK / kWaves;   // key rows each wave stages per
 // LDS: key and value tiles are row-major [64 keys][d] with no padding, so one direct-load
 // wave instruction (a contiguous 1 KB run) fills whole rows; the 16-byte chunks of each
 // row are XOR-swizzled (kswz, vswz) so that the operand reads hit distinct banks.
+constexpr int kWin = 256;   // plan entries (and their pages) staged in LDS at a time
+
 template <int HD>
 struct AttnSmem {
   uint16_t k[kStages][kTileK * HD];
   uint16_t v[kStages][kTileK * HD];
   int kblk[kStages][kTileK];       // block id of each key of a partial tile
+  int win_e[kWin];                 // the item's plan entries, one window at a time
+  int win_pg[kWin][kWaves];        // page of each 8-row group of those tiles (cached tiles)
 };
 
 // K operand reads: 16 lanes read rows r..r+15 at one logical chunk, so the swizzle spreads
@@ -117,8 +121,10 @@ __device__ __forceinline__ int tile_valid(const AttnArgs& a, const Item& it, int
 }
 
 // Staging state of one key tile for one wave. Lookup resolves the physical page of the
-// wave's 8 rows: a wave-uniform scalar load when the page size is a multiple of 8, one
-// vector load per lane and row otherwise.
+// wave's 8 rows: from the page ids staged in LDS with the item's plan window when the page
+// size is a multiple of 8, one vector load per lane and row otherwise. (The loop issues no
+// scalar memory loads: those share a wait counter with LDS reads and, returning out of
+// order, would make every LDS operand wait as long as a page-table miss.)
 template <int NI>
 struct Stage {
   int e;              // plan entry: (tile << 1) | is_partial; -1 when there is no tile
@@ -127,8 +133,10 @@ struct Stage {
   int krow;           // raw page id of row 8*wave + lane, lanes < 8 (per-lane path, block ids)
 };
 
+// `e` is the entry at window position `wi` (-1: no tile).
 template <int HD, int NI>
-__device__ __forceinline__ void stage_lookup(const AttnArgs& a, const Item& it, int e, Stage<NI>& st) {
+__device__ __forceinline__ void stage_lookup(const AttnArgs& a, const Item& it, int e, int wi,
+                                             const AttnSmem<HD>& sm, Stage<NI>& st) {
   using D = DmaShape<HD>;
   st.e = e;
   if (e < 0) return;
@@ -136,10 +144,7 @@ __device__ __forceinline__ void stage_lookup(const AttnArgs& a, const Item& it, 
   if (vt >= a.nct) return;                        // live tile: rows follow from the index
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (a.page_size % kRowsPerWave == 0) {
-    cint32* pt = as_const(a.page_table) + (int64_t)it.s * a.max_pages;
-    int lp, slot;
-    page_split(vt * kTileK + kRowsPerWave * wave, a.page_size, a.page_shift, &lp, &slot);
-    st.pw = pt[min(lp, a.max_pages - 1)];
+    st.pw = sm.win_pg[wi][wave];
   } else {
     const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
 #pragma unroll
@@ -288,8 +293,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     live_rows(a.cu_q, it.s, a.total_q, a.max_q_len, &it.q0, &it.q_len);
     it.kvl = clampi(a.kv_len[it.s], 0, a.max_pages * a.page_size);
     const int i0 = r * a.tile_q;
-    cint32* list = plan + L.list + (int64_t)u * a.nkt;
-    auto entry = [&](int o) { return o < oe ? (int)list[o] : -1; };
+    const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;
 
     // Query fragments of this lane's column (B operand of S^T = K Q^T), held in registers
     // for the whole item; padding rows read zeros.
@@ -312,29 +316,49 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.f;
     int n_partial = 0;
 
-    __syncthreads();   // the previous item's reads of LDS are finished
-    // Pipeline prologue: tiles ob and ob+1 in flight, ob+2 resolved.
+    // The item's tiles are processed in windows of kWin plan entries: the window's entries
+    // and, for cached tiles, the page of each 8-row group are staged in LDS first, so the
+    // tile loop reads its metadata from LDS only.
+    for (int wb = ob; wb < oe; wb += kWin) {
+      const int we = min(oe, wb + kWin);
+      __syncthreads();   // earlier readers of LDS (previous window or item) are finished
+      for (int i = tid; i < we - wb; i += kThreads) {
+        const int e = list[wb + i];
+        sm.win_e[i] = e;
+        const int vt = e >> 1;
+        if (vt < a.nct && a.page_size % kRowsPerWave == 0) {
+          const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
+#pragma unroll
+          for (int q = 0; q < kWaves; ++q) {
+            int lp, slot;
+            page_split(vt * kTileK + kRowsPerWave * q, a.page_size, a.page_shift, &lp, &slot);
+            sm.win_pg[i][q] = pt[min(lp, a.max_pages - 1)];
+          }
+        }
+      }
+      __syncthreads();
+      auto entry = [&](int o) { return o < we ? sm.win_e[o - wb] : -1; };
+
+    // Pipeline prologue: tiles wb and wb+1 in flight, wb+2 resolved.
     Stage<NI> s1, s2;
-    int e_cur = entry(ob);
-    stage_lookup<HD, NI>(a, it, e_cur, s1);
-    const int e1 = entry(ob + 1);
-    stage_lookup<HD, NI>(a, it, e1, s2);
-    if (e_cur >= 0) stage_fetch<HD, NI>(a, it, s1, sm, ob % kStages);
+    int e_cur = entry(wb);
+    stage_lookup<HD, NI>(a, it, e_cur, 0, sm, s1);
+    const int e1 = entry(wb + 1);
+    stage_lookup<HD, NI>(a, it, e1, 1, sm, s2);
+    if (e_cur >= 0) stage_fetch<HD, NI>(a, it, s1, sm, wb % kStages);
     const bool extra1 = (e1 >= 0) && (e1 & 1) && a.mode_b;   // block-id copy
-    if (e1 >= 0) stage_fetch<HD, NI>(a, it, s2, sm, (ob + 1) % kStages);
-    stage_lookup<HD, NI>(a, it, entry(ob + 2), s1);
-    int e_far = entry(ob + 3);
+    if (e1 >= 0) stage_fetch<HD, NI>(a, it, s2, sm, (wb + 1) % kStages);
+    stage_lookup<HD, NI>(a, it, entry(wb + 2), 2, sm, s1);
     land_tile<HD>(e1 >= 0, extra1);
 
-    for (int oi = ob; oi < oe; ++oi) {
+    for (int oi = wb; oi < we; ++oi) {
       const int sg = oi % kStages;
       const bool partial = e_cur & 1;
       const int e_next = entry(oi + 1);
       const int e_ahead = s1.e;                 // tile oi+2, rows resolved
       const bool extra = (e_ahead >= 0) && (e_ahead & 1) && a.mode_b;
       if (e_ahead >= 0) stage_fetch<HD, NI>(a, it, s1, sm, (oi + 2) % kStages);
-      stage_lookup<HD, NI>(a, it, e_far, s1);   // tile oi+3
-      e_far = entry(oi + 4);
+      stage_lookup<HD, NI>(a, it, entry(oi + 3), oi + 3 - wb, sm, s1);   // tile oi+3
       n_partial += partial;
       const uint16_t* kt = sm.k[sg];
       const uint16_t* vt = sm.v[sg];
@@ -343,9 +367,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       // S^T = K Q^T: two 32-key blocks x this wave's 32 query columns.
       f32x16 sc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int kb = 0; kb < 2; ++kb) {      // alternate the two accumulators
           const bf16x8 kf = *(const bf16x8*)&kt[koff[t] + 32 * kb * HD];
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], t == 0 ? f32x16{} : sc[kb], 0, 0, 0);
         }
@@ -405,11 +429,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       // keys 32kb+16hs + {4hl..4hl+3, 8+4hl..8+4hl+3} (its score registers), which two
       // transpose reads deliver as the A operand, for d = 32db + lane%32.
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
+          for (int db = 0; db < NDB; ++db) {    // consecutive steps use independent accumulators
             const int rofs = (32 * kb + 16 * hs) * HD;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs]);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs + 8 * HD]);
@@ -422,6 +446,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       land_tile<HD>(e_ahead >= 0, extra);
       e_cur = e_next;
     }
+    }   // window
 
     // Epilogue. Lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4.
     const float lt = l + __shfl_xor(l, 32);
