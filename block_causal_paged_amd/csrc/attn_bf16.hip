@@ -32,6 +32,8 @@
 // is a multiple of 8).
 #include "bcp_internal.h"
 
+#include <type_traits>
+
 namespace bcp {
 namespace {
 
@@ -42,6 +44,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -49,21 +52,29 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 3;
+constexpr int kKStages = 3;                     // key tile ring
+constexpr int kVStages = 4;                     // value tile (and key block id) ring
 constexpr int kRowsPerWave = kTileK / kWaves;   // key rows each wave stages per tile
 
 // LDS: key and value tiles are row-major [64 keys][d] with no padding, so one direct-load
 // wave instruction (a contiguous 1 KB run) fills whole rows; the 16-byte chunks of each
 // row are XOR-swizzled (kswz, vswz) so that the operand reads hit distinct banks.
-constexpr int kWin = 256;   // plan entries (and their pages) staged in LDS at a time
+// The item's plan entries and the physical pages of their key rows are staged in LDS one
+// window at a time: kWin tiles with one page per 8-row group when the page size is a
+// multiple of 8, else kWinRows tiles with one page per row.
+constexpr int kWin = 256;
+constexpr int kWinRows = kWin * kWaves / kTileK;
 
 template <int HD>
 struct AttnSmem {
-  uint16_t k[kStages][kTileK * HD];
-  uint16_t v[kStages][kTileK * HD];
-  int kblk[kStages][kTileK];       // block id of each key of a partial tile
+  uint16_t k[kKStages][kTileK * HD];
+  uint16_t v[kVStages][kTileK * HD];
+  int kblk[kVStages][kTileK];      // block id of each key of a partial tile
   int win_e[kWin];                 // the item's plan entries, one window at a time
-  int win_pg[kWin][kWaves];        // page of each 8-row group of those tiles (cached tiles)
+  union {
+    int grp[kWin][kWaves];         // page of each 8-row group of those tiles (cached tiles)
+    int row[kWinRows][kTileK];     // page of each row (cached tiles, other page sizes)
+  } win_pg;
 };
 
 // K operand reads: 16 lanes read rows r..r+15 at one logical chunk, so the swizzle spreads
@@ -82,24 +93,47 @@ __device__ __forceinline__ int vswz(int r) { return HD == 128 ? 4 * (r & 3) : 4 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+__device__ __forceinline__ unsigned uni(unsigned x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const void* uni(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  return (const void*)(uintptr_t)((uint64_t)uni((unsigned)x) | ((uint64_t)uni((unsigned)(x >> 32)) << 32));
+}
+// Per-lane 64-bit address.
 __device__ __forceinline__ void dma16(const void* g, unsigned lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(uni(lds)), "v"(g) : "memory");
+}
+// Wave-uniform base plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* base, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(uni(lds)), "v"(off), "s"(uni(base)) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, unsigned lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(uni(lds)), "v"(g) : "memory");
 }
-// Wait until at most N of this wave's vector-memory loads are outstanding (they complete
-// in issue order, so everything issued before the last N has landed).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+// Wait until at most n of this wave's vector-memory loads are outstanding (they complete
+// in issue order, so everything issued before the last n has landed). n is 0, 2*NI or
+// 2*NI + 1 (a tile's loads), NI being 1 or 2.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+  }
+}
+
+// Scheduling pattern for the matrix phase: after AHEAD LDS reads, each of the NM matrix
+// instructions is followed by its share of the remaining NR - AHEAD reads.
+template <int NM, int NR, int AHEAD, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int lo = AHEAD + (I * (NR - AHEAD)) / NM, hi = AHEAD + ((I + 1) * (NR - AHEAD)) / NM;
+    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);
+    interleave<NM, NR, AHEAD, I + 1>();
+  }
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
@@ -120,99 +154,133 @@ __device__ __forceinline__ int tile_valid(const AttnArgs& a, const Item& it, int
   return vt < a.nct ? clampi(it.kvl - vt * kTileK, 0, kTileK) : clampi(it.q_len - (vt - a.nct) * kTileK, 0, kTileK);
 }
 
-// Staging state of one key tile for one wave. Lookup resolves the physical page of the
-// wave's 8 rows: from the page ids staged in LDS with the item's plan window when the page
-// size is a multiple of 8, one vector load per lane and row otherwise. (The loop issues no
-// scalar memory loads: those share a wait counter with LDS reads and, returning out of
-// order, would make every LDS operand wait as long as a page-table miss.)
-template <int NI>
+// Staging state of one key tile for one wave. Lookup resolves the physical pages of the
+// wave's 8 rows from the page ids staged in LDS with the item's plan window: one page for
+// all 8 when the page size is a multiple of 8, else one per row. (The loop issues no
+// memory loads besides the tiles' own: scalar loads share a wait counter with LDS reads
+// and return out of order, and a vector load's wait would also wait for every tile in
+// flight.)
 struct Stage {
   int e;              // plan entry: (tile << 1) | is_partial; -1 when there is no tile
   int pw;             // page of this wave's rows (scalar path)
-  int row[NI];        // raw page id per staged row (per-lane path)
   int krow;           // raw page id of row 8*wave + lane, lanes < 8 (per-lane path, block ids)
+  i32x2 row;          // raw page id per staged row, NI <= 2 of them (per-lane path)
 };
 
-// `e` is the entry at window position `wi` (-1: no tile).
+// `e` is the entry at window position `wi` (-1: no tile). Every field is written exactly
+// once, at the end, so the state stays in registers.
 template <int HD, int NI>
-__device__ __forceinline__ void stage_lookup(const AttnArgs& a, const Item& it, int e, int wi,
-                                             const AttnSmem<HD>& sm, Stage<NI>& st) {
+__device__ __forceinline__ Stage stage_lookup(const AttnArgs& a, const Item& it, int e, int wi,
+                                              const AttnSmem<HD>& sm) {
   using D = DmaShape<HD>;
-  st.e = e;
-  if (e < 0) return;
-  const int vt = e >> 1;
-  if (vt >= a.nct) return;                        // live tile: rows follow from the index
+  static_assert(NI <= 2, "per-lane page ids hold at most two rows");
+  const int eu = uni(e);
+  const int vt = eu >> 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (a.page_size % kRowsPerWave == 0) {
-    st.pw = sm.win_pg[wi][wave];
-  } else {
-    const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
+  int pw = -1, krow = -1;
+  i32x2 row = {-1, -1};
+  if (eu >= 0 && vt < a.nct) {                     // live tiles: rows follow from the index
+    if (a.page_size % kRowsPerWave == 0) {
+      pw = uni(sm.win_pg.grp[wi][wave]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int j = vt * kTileK + kRowsPerWave * wave + k * D::RPI + lane / D::CPR;
-      int lp, slot;
-      page_split(j, a.page_size, a.page_shift, &lp, &slot);
-      st.row[k] = pt[min(lp, a.max_pages - 1)];
-    }
-    if ((e & 1) && a.mode_b) {
-      int lp, slot;
-      page_split(vt * kTileK + kRowsPerWave * wave + (lane & 7), a.page_size, a.page_shift, &lp, &slot);
-      st.krow = pt[min(lp, a.max_pages - 1)];
+      for (int k = 0; k < NI; ++k) row[k] = sm.win_pg.row[wi][kRowsPerWave * wave + k * D::RPI + lane / D::CPR];
+      if ((eu & 1) && a.mode_b) krow = sm.win_pg.row[wi][kRowsPerWave * wave + (lane & 7)];
     }
   }
+  Stage st;
+  st.e = eu;
+  st.pw = pw;
+  st.krow = krow;
+  st.row = row;
+  return st;
 }
 
-// Issue the direct loads of a resolved tile into LDS stage `sg`: NI K and NI V wave
-// instructions per wave, plus one block-id copy on wave 0 for partial mode-B tiles. An
-// absent key (past its region's length, or in a page outside the pool) copies the
-// sequence's first live row: absent keys only occur in partial tiles, where the mask
-// gives them weight exactly 0, and that row is finite, so it adds exactly nothing.
+// Per-lane byte offsets of the fast staging path: row k*RPI + lane/CPR of the wave's 8-row
+// run, at the swizzled chunk, relative to the run's first row.
+template <int HD>
+struct FastOffsets {
+  unsigned k[DmaShape<HD>::NI], v[DmaShape<HD>::NI];
+};
+
+// Issue the direct loads of a resolved tile into key stage `sk` and value stage `sv`: NI K
+// and NI V wave instructions per wave, plus one block-id copy per wave for partial mode-B
+// tiles. Returns the number of loads issued. A full tile whose 8 rows per wave are
+// consecutive in memory (a cached tile in pages of a multiple of 8 rows, or a live tile)
+// takes one wave-uniform base and fixed per-lane offsets. Otherwise each lane forms its own
+// address, and an absent key (past its region's length, or in a page outside the pool)
+// copies the sequence's first live row: absent keys only occur in partial tiles, where the
+// mask gives them weight exactly 0, and that row is finite, so it adds exactly nothing.
 template <int HD, int NI>
-__device__ __forceinline__ void stage_fetch(const AttnArgs& a, const Item& it, const Stage<NI>& st,
-                                            AttnSmem<HD>& sm, int sg) {
+__device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st,
+                                           AttnSmem<HD>& sm, int sk, int sv, const FastOffsets<HD>& fo) {
   using D = DmaShape<HD>;
+  if (st.e < 0) return 0;
   const int vt = st.e >> 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const bool cached = vt < a.nct;
   const int nvalid = tile_valid(a, it, vt);
   const uint16_t* kb = (const uint16_t*)(cached ? a.k_cache : a.k_new);
   const uint16_t* vb = (const uint16_t*)(cached ? a.v_cache : a.v_new);
-  const int64_t sub = ((int64_t)it.q0 * a.Hkv + it.g) * HD;   // substitute row for absent keys
   const bool scalar_pages = a.page_size % kRowsPerWave == 0;
-#pragma unroll
-  for (int k = 0; k < NI; ++k) {
-    const int r = kRowsPerWave * wave + k * D::RPI + lane / D::CPR;   // row inside the tile
-    const int pch = lane % D::CPR;                                     // physical chunk
-    int64_t row = -1;
-    if (r < nvalid) {
-      if (cached) {
-        const int p = scalar_pages ? st.pw : st.row[k];
-        if (p >= 0 && p < a.num_pages) {
-          int lp, slot;
-          page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
-          row = (int64_t)p * a.page_size + slot;
-        }
-      } else {
-        row = it.q0 + (vt - a.nct) * kTileK + r;
-      }
+  const int run0 = kRowsPerWave * wave;           // first tile row of this wave
+  const bool fast = nvalid == kTileK && (!cached || (scalar_pages && (unsigned)st.pw < (unsigned)a.num_pages));
+  if (fast) {
+    int64_t row0;
+    if (cached) {
+      int lp, slot;
+      page_split(vt * kTileK + run0, a.page_size, a.page_shift, &lp, &slot);
+      row0 = (int64_t)st.pw * a.page_size + slot;
+    } else {
+      row0 = it.q0 + (int64_t)(vt - a.nct) * kTileK + run0;
     }
-    const bool ok = row >= 0;
-    const uint16_t* ksrc = ok ? kb + (row * a.Hkv + it.g) * HD : (const uint16_t*)a.k_new + sub;
-    const uint16_t* vsrc = ok ? vb + (row * a.Hkv + it.g) * HD : (const uint16_t*)a.v_new + sub;
-    const int base = (kRowsPerWave * wave + k * D::RPI) * HD;
-    dma16(ksrc + 8 * (pch ^ kswz<HD>(r)), lds_addr(&sm.k[sg][base]));
-    dma16(vsrc + 8 * (pch ^ vswz<HD>(r)), lds_addr(&sm.v[sg][base]));
+    const int64_t e0 = (row0 * a.Hkv + it.g) * HD;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int base = (run0 + k * D::RPI) * HD;
+      dma16s(kb + e0, fo.k[k], lds_addr(&sm.k[sk][base]));
+      dma16s(vb + e0, fo.v[k], lds_addr(&sm.v[sv][base]));
+    }
+  } else {
+    const int64_t sub = ((int64_t)it.q0 * a.Hkv + it.g) * HD;   // substitute row for absent keys
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int r = run0 + k * D::RPI + lane / D::CPR;   // row inside the tile
+      const int pch = lane % D::CPR;                     // physical chunk
+      int64_t row = -1;
+      if (r < nvalid) {
+        if (cached) {
+          const int p = scalar_pages ? st.pw : st.row[k];   // values, not addresses
+          if (p >= 0 && p < a.num_pages) {
+            int lp, slot;
+            page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
+            row = (int64_t)p * a.page_size + slot;
+          }
+        } else {
+          row = it.q0 + (vt - a.nct) * kTileK + r;
+        }
+      }
+      const bool ok = row >= 0;
+      const uint16_t* ksrc = ok ? kb + (row * a.Hkv + it.g) * HD : (const uint16_t*)a.k_new + sub;
+      const uint16_t* vsrc = ok ? vb + (row * a.Hkv + it.g) * HD : (const uint16_t*)a.v_new + sub;
+      const int base = (run0 + k * D::RPI) * HD;
+      dma16(ksrc + 8 * (pch ^ kswz<HD>(r)), lds_addr(&sm.k[sk][base]));
+      dma16(vsrc + 8 * (pch ^ vswz<HD>(r)), lds_addr(&sm.v[sv][base]));
+    }
   }
   // Block ids of a partial tile's keys: each wave handles its own 8 rows (lanes 0..7).
   // Mode A needs no memory; mode B copies them with an exec-masked 4-byte direct load
   // (inactive lanes issue no request); keys past nvalid are masked separately.
   if (st.e & 1) {
-    const int r = kRowsPerWave * wave + (lane & 7);
+    const int r = run0 + (lane & 7);
     const int j = (cached ? vt : vt - a.nct) * kTileK + r;
     if (!a.mode_b) {
-      if (lane < 8) sm.kblk[sg][r] = r >= nvalid ? kNoKeyBlk : (cached ? kNegInfBlk : j / a.block_size);
+      if (lane < 8) sm.kblk[sv][r] = r >= nvalid ? kNoKeyBlk : (cached ? kNegInfBlk : j / a.block_size);
     } else {
-      const int32_t* src = a.q_blk + it.q0;                    // in bounds, used when absent
+      // Keys that exist take their id from memory (a key in a page outside the pool gets
+      // the sequence's first live row's id: its K and V were substituted by that row, so
+      // it adds exactly nothing whatever its weight); absent keys get the id nobody sees.
+      const int32_t* src = a.q_blk + it.q0;
       if (r < nvalid) {
         if (cached) {
           int lp, slot;
@@ -223,23 +291,29 @@ __device__ __forceinline__ void stage_fetch(const AttnArgs& a, const Item& it, c
           src = a.q_blk + it.q0 + j;
         }
       }
-      if (lane < 8) dma4(src, lds_addr(&sm.kblk[sg][kRowsPerWave * wave]));
+      if (lane < 8 && r >= nvalid) sm.kblk[sv][r] = kNoKeyBlk;
+      if (lane < 8 && r < nvalid) dma4(src, lds_addr(&sm.kblk[sv][run0]));
+      return 2 * NI + 1;
     }
   }
+  return 2 * NI;
 }
 
-// Publish a tile: this wave's loads of it have landed once at most the loads issued after
-// it (the next tile's: 2*NI, plus the block-id copy of a partial mode-B tile) are
-// outstanding; then the workgroup barrier makes every wave's share visible.
-template <int HD>
-__device__ __forceinline__ void land_tile(bool next_in_flight, bool next_extra) {
-  constexpr int per = 2 * DmaShape<HD>::NI;
-  if (!next_in_flight) wait_vm<0>();
-  else if (next_extra) wait_vm<per + 1>();
-  else wait_vm<per>();
-  __syncthreads();
-}
-
+// Wave schedule. The 8 waves form two groups, A = waves 0-3 and B = waves 4-7, one wave
+// of each per SIMD. Each tile t is handled in two phases per wave: a matrix phase
+// (S(t) = K(t) Q^T, then O += V(t-1) P(t-1)) and a vector phase (mask, online softmax
+// of S(t) into P(t), issuing loads, waiting for its own loads). Workgroup barriers split
+// time into half-steps H0, H1, ...; group A runs the matrix phase of tile t in H(2t) and
+// the vector phase in H(2t+1), group B one half-step later, so on every SIMD one wave's
+// matrix instructions run beside the other wave's vector instructions.
+//
+// Loads: a wave of group A issues its share of tile t+2 in its vector phase of tile t
+// (half-step H(2t+1)), a wave of group B its share of tile t+3 (H(2t+2)); each then waits
+// until only that newest tile is still in flight. So tile x is issued in H(2x-4) and
+// H(2x-3) and complete and visible at the barrier that starts H(2x), when group A first
+// reads it. K(x) is last read in H(2x+1), V(x) and the block ids of x in H(2x+3), all before
+// the loads of tile x+3 (keys) or x+4 (values) start in H(2x+2) or later: three key
+// stages and four value stages suffice.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   using D = DmaShape<HD>;
@@ -250,6 +324,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hl = lane >> 5;
+  const int grp = uni(wave) >> 2;   // 0: group A, 1: group B (scalar: guards barriers)
+  const int lead = 2 + grp;         // tiles ahead of the current one that this wave issues
   const int G = a.G;
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
   cint32* plan = as_const(a.plan);
@@ -278,6 +354,13 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       const int dcol = 32 * db + vcol0;
       voff[db] = vrow0 * HD + ((dcol >> 3) ^ vs) * 8 + (dcol & 7);
     }
+  }
+  FastOffsets<HD> fo;
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int rr = k * D::RPI + lane / D::CPR, r = kRowsPerWave * wave + rr, pch = lane % D::CPR;
+    fo.k[k] = (unsigned)(((int64_t)rr * a.Hkv * HD + 8 * (pch ^ kswz<HD>(r))) * 2);
+    fo.v[k] = (unsigned)(((int64_t)rr * a.Hkv * HD + 8 * (pch ^ vswz<HD>(r))) * 2);
   }
   if (a.stats && blockIdx.x == 0 && tid == 0)   // skipped tiles of the whole grid, per kv head
     atomicAdd(&a.stats[2], (unsigned long long)a.Hkv * ((unsigned long long)L.units * a.nkt - plan[3]));
@@ -309,6 +392,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     const int qblk = !qvalid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[it.q0 + pos] : pos / a.block_size);
+    // Consume the loads here, so that no wait for them lands inside the tile loop (where it
+    // would also wait for every tile in flight).
+#pragma unroll
+    for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(qf[t]));
+    asm volatile("" ::"v"(qblk));
 
     f32x16 o[NDB];
 #pragma unroll
@@ -316,136 +404,185 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.f;
     int n_partial = 0;
 
-    // The item's tiles are processed in windows of kWin plan entries: the window's entries
-    // and, for cached tiles, the page of each 8-row group are staged in LDS first, so the
-    // tile loop reads its metadata from LDS only.
-    for (int wb = ob; wb < oe; wb += kWin) {
-      const int we = min(oe, wb + kWin);
+    // The item's tiles are processed in windows: the window's plan entries and the pages of
+    // its cached tiles are staged in LDS first, so the tile loop reads its metadata from
+    // LDS only and issues no memory loads but the tiles' own.
+    const bool grp_pages = a.page_size % kRowsPerWave == 0;
+    const int win = grp_pages ? kWin : kWinRows;
+    for (int wb = ob; wb < oe; wb += win) {
+      const int nt = min(oe - wb, win);      // tiles in this window
       __syncthreads();   // earlier readers of LDS (previous window or item) are finished
-      for (int i = tid; i < we - wb; i += kThreads) {
-        const int e = list[wb + i];
-        sm.win_e[i] = e;
-        const int vt = e >> 1;
-        if (vt < a.nct && a.page_size % kRowsPerWave == 0) {
-          const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
-#pragma unroll
-          for (int q = 0; q < kWaves; ++q) {
+      const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
+      for (int i = tid; i < nt; i += kThreads) sm.win_e[i] = list[wb + i];
+      if (grp_pages) {
+        for (int i = tid; i < nt * kWaves; i += kThreads) {
+          const int vt = list[wb + i / kWaves] >> 1, q = i % kWaves;
+          if (vt < a.nct) {
             int lp, slot;
             page_split(vt * kTileK + kRowsPerWave * q, a.page_size, a.page_shift, &lp, &slot);
-            sm.win_pg[i][q] = pt[min(lp, a.max_pages - 1)];
+            sm.win_pg.grp[i / kWaves][q] = pt[min(lp, a.max_pages - 1)];
+          }
+        }
+      } else {
+        for (int i = tid; i < nt * kTileK; i += kThreads) {
+          const int vt = list[wb + i / kTileK] >> 1, r = i % kTileK;
+          if (vt < a.nct) {
+            int lp, slot;
+            page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
+            sm.win_pg.row[i / kTileK][r] = pt[min(lp, a.max_pages - 1)];
           }
         }
       }
       __syncthreads();
-      auto entry = [&](int o) { return o < we ? sm.win_e[o - wb] : -1; };
+      auto entry = [&](int t) { return t < nt ? sm.win_e[t] : -1; };
 
-    // Pipeline prologue: tiles wb and wb+1 in flight, wb+2 resolved.
-    Stage<NI> s1, s2;
-    int e_cur = entry(wb);
-    stage_lookup<HD, NI>(a, it, e_cur, 0, sm, s1);
-    const int e1 = entry(wb + 1);
-    stage_lookup<HD, NI>(a, it, e1, 1, sm, s2);
-    if (e_cur >= 0) stage_fetch<HD, NI>(a, it, s1, sm, wb % kStages);
-    const bool extra1 = (e1 >= 0) && (e1 & 1) && a.mode_b;   // block-id copy
-    if (e1 >= 0) stage_fetch<HD, NI>(a, it, s2, sm, (wb + 1) % kStages);
-    stage_lookup<HD, NI>(a, it, entry(wb + 2), 2, sm, s1);
-    land_tile<HD>(e1 >= 0, extra1);
-
-    for (int oi = wb; oi < we; ++oi) {
-      const int sg = oi % kStages;
-      const bool partial = e_cur & 1;
-      const int e_next = entry(oi + 1);
-      const int e_ahead = s1.e;                 // tile oi+2, rows resolved
-      const bool extra = (e_ahead >= 0) && (e_ahead & 1) && a.mode_b;
-      if (e_ahead >= 0) stage_fetch<HD, NI>(a, it, s1, sm, (oi + 2) % kStages);
-      stage_lookup<HD, NI>(a, it, entry(oi + 3), oi + 3 - wb, sm, s1);   // tile oi+3
-      n_partial += partial;
-      const uint16_t* kt = sm.k[sg];
-      const uint16_t* vt = sm.v[sg];
-      const int nvalid = tile_valid(a, it, e_cur >> 1);
-
-      // S^T = K Q^T: two 32-key blocks x this wave's 32 query columns.
-      f32x16 sc[2];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {      // alternate the two accumulators
-          const bf16x8 kf = *(const bf16x8*)&kt[koff[t] + 32 * kb * HD];
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], t == 0 ? f32x16{} : sc[kb], 0, 0, 0);
-        }
+      // Prologue: tiles 0 .. lead-1 issued; this wave waits for all of them but the last
+      // (group A: tile 0; group B: tiles 0 and 1), then tile 0 is published.
+      Stage st;
+      int issued = 0;
+      for (int x = 0; x < lead; ++x) {
+        st = stage_lookup<HD, NI>(a, it, entry(x), x, sm);
+        issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo);
       }
+      st = stage_lookup<HD, NI>(a, it, entry(lead), lead, sm);
+      wait_vm(issued);
+      __syncthreads();
+      if (grp) __syncthreads();           // group B starts half a step later
 
-      // Mask, only on partial tiles. Lane (col, hl) holds key 32kb + 8(v/4) + 4hl + v%4.
-      if (partial) {
+      bf16x8 pf[2][2];
+      f32x16 sc[2];
+      // Matrix phase: O^T += V^T P^T for tile t-1 (when WITH_PV), then S^T(t) = K Q^T for
+      // two 32-key blocks x this wave's 32 query columns (when WITH_S). Operand reads run a
+      // few steps ahead of the matrix instructions that consume them.
+      auto matrix_phase = [&](int t, auto with_s, auto with_pv) {
+        constexpr bool WITH_S = decltype(with_s)::value, WITH_PV = decltype(with_pv)::value;
+        if constexpr (WITH_PV) {
+          // Step (kb, hs) covers keys 32kb+16hs .. +15; lane half hl feeds the keys
+          // 32kb+16hs + {4hl..4hl+3, 8+4hl..8+4hl+3} (its score registers), which two
+          // transpose reads deliver as the A operand, for d = 32db + lane%32.
+          const uint16_t* vt = sm.v[(t - 1) % kVStages];
+          bf16x8 vf[2][2][NDB];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const int rofs = (32 * kb + 16 * hs) * HD;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs]);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs + 8 * HD]);
+                vf[kb][hs][db] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+              for (int db = 0; db < NDB; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][hs][db], pf[kb][hs], o[db], 0, 0, 0);
+        }
+        if constexpr (WITH_S) {
+          const uint16_t* kt = sm.k[t % kKStages];
+          bf16x8 kf[NT][2];
+#pragma unroll
+          for (int s = 0; s < NT; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) kf[s][kb] = *(const bf16x8*)&kt[koff[s] + 32 * kb * HD];
+#pragma unroll
+          for (int s = 0; s < NT; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)      // alternate the two accumulators
+              sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][kb], qf[s], s == 0 ? f32x16{} : sc[kb], 0, 0, 0);
+        }
+        // Interleave: a few operand reads first, then one matrix instruction per read
+        // (K: one b128 read per instruction; V: two transpose reads per instruction).
+        constexpr int NR = (WITH_S ? 2 * NT : 0) + (WITH_PV ? 8 * NDB : 0);
+        constexpr int NM = (WITH_S ? 2 * NT : 0) + (WITH_PV ? 4 * NDB : 0);
+        constexpr int AHEAD = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+        interleave<NM, NR, AHEAD>();
+      };
+
+      // Vector phase of tile t: issue this wave's loads of tile t+lead and resolve the tile
+      // after it, then mask (partial tiles only) and the online softmax of S(t) into P(t),
+      // then wait until only the tile just issued is in flight.
+      auto vector_phase = [&](int t) {
+        {
+          const int x = t + lead;
+          issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo);
+          st = stage_lookup<HD, NI>(a, it, entry(x + 1), x + 1, sm);
+        }
+        // Lane (col, hl) holds key 32kb + 8(v/4) + 4hl + v%4.
+        const int e_t = entry(t);
+        const bool partial = e_t & 1;
+        n_partial += partial;
+        if (partial) {   // absent keys carry kNoKeyBlk, which no row sees
+          const int* kbl = sm.kblk[t % kVStages] + 4 * hl;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const i32x4 kbw = *(const i32x4*)&kbl[32 * kb + 8 * v4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (kbw[c] > qblk) sc[kb][4 * v4 + c] = -INFINITY;
+            }
+        }
+        // Online softmax in the log2 domain, with a lazy reference max: m only moves when
+        // a row's max grows by more than 2^8 (or on its first visible key). Numerator and
+        // denominator both use m, so the result is the same; P <= 2^8 fits bf16 easily.
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int k0 = 32 * kb + 8 * v4 + 4 * hl;
-            const i32x4 kbw = *(const i32x4*)&sm.kblk[sg][k0];
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mcand = mx * sl2;
+        const bool grow = mcand > m + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          // Rows that do not grow keep alpha = 1 (their m may still be -inf).
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m - mcand) : 1.f;   // 0 if m was -inf
+          m = grow ? mcand : m;
+          l *= alpha;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (kbw[c] > qblk || k0 + c >= nvalid) sc[kb][4 * v4 + c] = -INFINITY;
-          }
-      }
-
-      // Online softmax in the log2 domain, with a lazy reference max: m only moves when a
-      // row's max grows by more than 2^8 (or on its first visible key). Numerator and
-      // denominator both use m, so the result is the same; P <= 2^8 fits bf16 easily.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mcand = mx * sl2;
-      const bool grow = mcand > m + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        // Rows that do not grow keep alpha = 1 (their m may still be -inf).
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mcand) : 1.f;   // 0 if m was -inf
-        m = grow ? mcand : m;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      const float muse = m == -INFINITY ? 0.f : m;
-      bf16x8 pf[2][2];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          f32x8 x;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hs + e], sl2, -muse));
-            rs += x[e];
-          }
-          pf[kb][hs] = to_bf16x8(x);
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
         }
-      l += rs;
-
-      // O^T += V^T P^T. Step (kb, hs) covers keys 32kb+16hs .. +15; lane half hl feeds the
-      // keys 32kb+16hs + {4hl..4hl+3, 8+4hl..8+4hl+3} (its score registers), which two
-      // transpose reads deliver as the A operand, for d = 32db + lane%32.
+        const float muse = m == -INFINITY ? 0.f : m;
+        // P in bf16; the row sum adds the fp32 values, as a tree per 8 keys.
+        float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
+          for (int hs = 0; hs < 2; ++hs) {
+            f32x8 x;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {    // consecutive steps use independent accumulators
-            const int rofs = (32 * kb + 16 * hs) * HD;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs]);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs + 8 * HD]);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hs], o[db], 0, 0, 0);
+            for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hs + e], sl2, -muse));
+            pf[kb][hs] = to_bf16x8(x);
+            rs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
           }
+        l += rs;
+        // Keep the softmax ahead of the wait below (the compiler may not sink it past).
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) asm volatile("" ::"v"(pf[kb][hs]));
+        asm volatile("" ::"v"(l));
+        wait_vm(issued);
+      };
 
-      // Tile oi+1 must have landed (for every wave) before the next iteration reads it;
-      // tile oi+2's loads may stay in flight.
-      land_tile<HD>(e_ahead >= 0, extra);
-      e_cur = e_next;
-    }
+      matrix_phase(0, std::true_type{}, std::false_type{});
+      __syncthreads();
+      vector_phase(0);
+      __syncthreads();
+      for (int t = 1; t < nt; ++t) {
+        matrix_phase(t, std::true_type{}, std::true_type{});
+        __syncthreads();
+        vector_phase(t);
+        __syncthreads();
+      }
+      // The last tile's PV product; group A then waits out group B's last vector phase.
+      matrix_phase(nt, std::false_type{}, std::true_type{});
+      if (!grp) __syncthreads();
     }   // window
 
     // Epilogue. Lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4.
@@ -480,6 +617,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 
     if (a.stats && tid == 0) {
       const int n = oe - ob;
+      // n_partial counts the tiles of wave 0 only: every wave sees every tile.
       atomicAdd(&a.stats[0], (unsigned long long)(n - n_partial));
       atomicAdd(&a.stats[1], (unsigned long long)n_partial);
       atomicAdd(&a.stats[3], (unsigned long long)n * 2ull * kTileK * HD * 2ull);

@@ -18,7 +18,8 @@ constexpr int kRowsPerWG = 256;
 // Split-KV planning. A unit is one (sequence, q-tile); its non-skipped key tiles are cut
 // into nearly equal chunks so that the step has about kTargetWGs (chunk, kv head) work
 // items in total, each at least kMinChunk tiles long. Proof of the bounds used for buffer
-// sizes: with c = max(kMinChunk, ceil(T*Hkv/kTargetWGs)) and T the non-skipped tile total,
+// sizes: with c >= max(kMinChunk, ceil(T*Hkv/kTargetWGs)) and T the non-skipped tile total
+// (the planner may lengthen c so that the items fit kTargetWGs exactly),
 // sum_u ceil(cnt_u/c) <= T/c + U <= kTargetWGs/Hkv + U items; a split unit has cnt_u > c,
 // so its ceil(cnt_u/c) < 2*cnt_u/c and all split items times Hkv stay below 2*kTargetWGs.
 constexpr int kTargetWGs = 256;

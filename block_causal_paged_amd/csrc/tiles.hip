@@ -49,6 +49,20 @@ __device__ int block_scan_excl(int v, int* lds16, int* total) {
   return before + x - v;
 }
 
+// Maximum of v over the workgroup (every thread gets it).
+__device__ int block_max(int v, int* lds16) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  if (lane == 0) lds16[wave] = x;
+  __syncthreads();
+  int all = lds16[0];
+  for (int w = 1; w < nw; ++w) all = max(all, lds16[w]);
+  __syncthreads();
+  return all;
+}
+
 __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
   __shared__ int red[2][4];
   __shared__ int scan_lds[16];
@@ -170,6 +184,30 @@ __global__ __launch_bounds__(1024) void planner_kernel(PlanArgs a) {
   const long long work = (long long)total_tiles * a.num_kv_heads;
   int chunk = (int)((work + kTargetWGs - 1) / kTargetWGs);
   chunk = max(chunk, kMinChunk);
+  // Rounding each unit up to whole chunks can leave slightly more than kTargetWGs work
+  // items, and the few left over would run as a second round after everything else. Take
+  // the smallest chunk length that keeps the item count within kTargetWGs when one exists
+  // (the count only falls as the chunk grows, so a bisection finds it).
+  {
+    int mx = 0;
+    for (int u = tid; u < units; u += blockDim.x) mx = max(mx, plan[L.cnt + u]);
+    const int cmax = block_max(mx, scan_lds);
+    auto fits = [&](int c) {
+      int p = 0, tot;
+      for (int u = tid; u < units; u += blockDim.x) p += (plan[L.cnt + u] + c - 1) / c;
+      block_scan_excl(p, scan_lds, &tot);
+      return (long long)tot * a.num_kv_heads <= kTargetWGs;
+    };
+    if (cmax > chunk && !fits(chunk) && fits(cmax)) {
+      int lo = chunk, hi = cmax;   // fits(lo) is false, fits(hi) is true
+      while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (fits(mid)) hi = mid;
+        else lo = mid;
+      }
+      chunk = hi;
+    }
+  }
 
   int item_carry = 0, slot_carry = 0, split_carry = 0;
   for (int base = 0; base < units; base += blockDim.x) {
