@@ -59,22 +59,17 @@ constexpr int kRowsPerWave = kTileK / kWaves;   // key rows each wave stages per
 // LDS: key and value tiles are row-major [64 keys][d] with no padding, so one direct-load
 // wave instruction (a contiguous 1 KB run) fills whole rows; the 16-byte chunks of each
 // row are XOR-swizzled (kswz, vswz) so that the operand reads hit distinct banks.
-// The item's plan entries and the physical pages of their key rows are staged in LDS one
-// window at a time: kWin tiles with one page per 8-row group when the page size is a
-// multiple of 8, else kWinRows tiles with one page per row.
+// The item's plan entries are staged in LDS one window of kWin tiles at a time, with, for
+// each tile and wave, the memory row of the wave's first key row when all 8 of its rows are
+// present and consecutive in memory (-1 otherwise).
 constexpr int kWin = 256;
-constexpr int kWinRows = kWin * kWaves / kTileK;
-
 template <int HD>
 struct AttnSmem {
   uint16_t k[kKStages][kTileK * HD];
   uint16_t v[kVStages][kTileK * HD];
   int kblk[kVStages][kTileK];      // block id of each key of a partial tile
   int win_e[kWin];                 // the item's plan entries, one window at a time
-  union {
-    int grp[kWin][kWaves];         // page of each 8-row group of those tiles (cached tiles)
-    int row[kWinRows][kTileK];     // page of each row (cached tiles, other page sizes)
-  } win_pg;
+  int win_row[kWin][kWaves];       // first memory row of each wave's 8 rows, or -1
 };
 
 // K operand reads: 16 lanes read rows r..r+15 at one logical chunk, so the swizzle spreads
@@ -136,6 +131,13 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// max(x[l % 32], x[l % 32 + 32]) in every lane l: the max over the two halves of the wave,
+// exchanged with a cross-half lane swap instead of an LDS round trip.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 
 struct Item {
@@ -154,45 +156,37 @@ __device__ __forceinline__ int tile_valid(const AttnArgs& a, const Item& it, int
   return vt < a.nct ? clampi(it.kvl - vt * kTileK, 0, kTileK) : clampi(it.q_len - (vt - a.nct) * kTileK, 0, kTileK);
 }
 
-// Staging state of one key tile for one wave. Lookup resolves the physical pages of the
-// wave's 8 rows from the page ids staged in LDS with the item's plan window: one page for
-// all 8 when the page size is a multiple of 8, else one per row. (The loop issues no
-// memory loads besides the tiles' own: scalar loads share a wait counter with LDS reads
-// and return out of order, and a vector load's wait would also wait for every tile in
-// flight.)
+// Staging state of one key tile for one wave: the plan entry and the memory row of the
+// wave's first key row (rows of the kv cache for a cached tile, of the new keys for a live
+// tile), -1 when the wave's rows need the general path.
 struct Stage {
   int e;              // plan entry: (tile << 1) | is_partial; -1 when there is no tile
-  int pw;             // page of this wave's rows (scalar path)
-  int krow;           // raw page id of row 8*wave + lane, lanes < 8 (per-lane path, block ids)
-  i32x2 row;          // raw page id per staged row, NI <= 2 of them (per-lane path)
+  int row0;
 };
 
-// `e` is the entry at window position `wi` (-1: no tile). Every field is written exactly
-// once, at the end, so the state stays in registers.
-template <int HD, int NI>
-__device__ __forceinline__ Stage stage_lookup(const AttnArgs& a, const Item& it, int e, int wi,
-                                              const AttnSmem<HD>& sm) {
-  using D = DmaShape<HD>;
-  static_assert(NI <= 2, "per-lane page ids hold at most two rows");
-  const int eu = uni(e);
-  const int vt = eu >> 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int pw = -1, krow = -1;
-  i32x2 row = {-1, -1};
-  if (eu >= 0 && vt < a.nct) {                     // live tiles: rows follow from the index
-    if (a.page_size % kRowsPerWave == 0) {
-      pw = uni(sm.win_pg.grp[wi][wave]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < NI; ++k) row[k] = sm.win_pg.row[wi][kRowsPerWave * wave + k * D::RPI + lane / D::CPR];
-      if ((eu & 1) && a.mode_b) krow = sm.win_pg.row[wi][kRowsPerWave * wave + (lane & 7)];
-    }
-  }
+// Tile metadata as read from LDS for window position wi. Reading only issues the LDS loads
+// (at a clamped, always valid position, so that no value has to be merged before it
+// arrives); they are used one phase later, so the loop never waits for them.
+struct RawMeta {
+  int e, row0;
+  bool valid;       // wi < nt
+};
+
+template <int HD>
+__device__ __forceinline__ RawMeta meta_read(int wi, int nt, const AttnSmem<HD>& sm) {
+  const int wave = threadIdx.x >> 6, w = min(wi, kWin - 1);
+  RawMeta r;
+  r.valid = wi < nt;
+  r.e = sm.win_e[w];
+  r.row0 = sm.win_row[w][wave];
+  return r;
+}
+
+// Make the entry and the row wave-uniform (they are the same in every lane).
+__device__ __forceinline__ Stage meta_resolve(const RawMeta& r) {
   Stage st;
-  st.e = eu;
-  st.pw = pw;
-  st.krow = krow;
-  st.row = row;
+  st.e = r.valid ? uni(r.e) : -1;
+  st.row0 = uni(r.row0);
   return st;
 }
 
@@ -205,12 +199,12 @@ struct FastOffsets {
 
 // Issue the direct loads of a resolved tile into key stage `sk` and value stage `sv`: NI K
 // and NI V wave instructions per wave, plus one block-id copy per wave for partial mode-B
-// tiles. Returns the number of loads issued. A full tile whose 8 rows per wave are
-// consecutive in memory (a cached tile in pages of a multiple of 8 rows, or a live tile)
-// takes one wave-uniform base and fixed per-lane offsets. Otherwise each lane forms its own
-// address, and an absent key (past its region's length, or in a page outside the pool)
-// copies the sequence's first live row: absent keys only occur in partial tiles, where the
-// mask gives them weight exactly 0, and that row is finite, so it adds exactly nothing.
+// tiles. Returns the number of loads issued. When the wave's 8 rows are present and
+// consecutive in memory (row0 >= 0), one wave-uniform base and fixed per-lane offsets
+// address them. Otherwise each lane resolves its own row through the page table, and an
+// absent key (past its region's length, or in a page outside the pool) copies the
+// sequence's first live row: absent keys only occur in partial tiles, where the mask gives
+// them weight exactly 0, and that row is finite, so it adds exactly nothing.
 template <int HD, int NI>
 __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st,
                                            AttnSmem<HD>& sm, int sk, int sv, const FastOffsets<HD>& fo) {
@@ -219,22 +213,11 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
   const int vt = st.e >> 1;
   const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const bool cached = vt < a.nct;
-  const int nvalid = tile_valid(a, it, vt);
   const uint16_t* kb = (const uint16_t*)(cached ? a.k_cache : a.k_new);
   const uint16_t* vb = (const uint16_t*)(cached ? a.v_cache : a.v_new);
-  const bool scalar_pages = a.page_size % kRowsPerWave == 0;
   const int run0 = kRowsPerWave * wave;           // first tile row of this wave
-  const bool fast = nvalid == kTileK && (!cached || (scalar_pages && (unsigned)st.pw < (unsigned)a.num_pages));
-  if (fast) {
-    int64_t row0;
-    if (cached) {
-      int lp, slot;
-      page_split(vt * kTileK + run0, a.page_size, a.page_shift, &lp, &slot);
-      row0 = (int64_t)st.pw * a.page_size + slot;
-    } else {
-      row0 = it.q0 + (int64_t)(vt - a.nct) * kTileK + run0;
-    }
-    const int64_t e0 = (row0 * a.Hkv + it.g) * HD;
+  if (st.row0 >= 0) {
+    const int64_t e0 = ((int64_t)st.row0 * a.Hkv + it.g) * HD;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int base = (run0 + k * D::RPI) * HD;
@@ -242,6 +225,8 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       dma16s(vb + e0, fo.v[k], lds_addr(&sm.v[sv][base]));
     }
   } else {
+    const int nvalid = tile_valid(a, it, vt);
+    const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
     const int64_t sub = ((int64_t)it.q0 * a.Hkv + it.g) * HD;   // substitute row for absent keys
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
@@ -250,12 +235,10 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       int64_t row = -1;
       if (r < nvalid) {
         if (cached) {
-          const int p = scalar_pages ? st.pw : st.row[k];   // values, not addresses
-          if (p >= 0 && p < a.num_pages) {
-            int lp, slot;
-            page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
-            row = (int64_t)p * a.page_size + slot;
-          }
+          int lp, slot;
+          page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
+          const int p = pt[min(lp, a.max_pages - 1)];
+          if (p >= 0 && p < a.num_pages) row = (int64_t)p * a.page_size + slot;
         } else {
           row = it.q0 + (vt - a.nct) * kTileK + r;
         }
@@ -270,8 +253,9 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
   }
   // Block ids of a partial tile's keys: each wave handles its own 8 rows (lanes 0..7).
   // Mode A needs no memory; mode B copies them with an exec-masked 4-byte direct load
-  // (inactive lanes issue no request); keys past nvalid are masked separately.
+  // (inactive lanes issue no request).
   if (st.e & 1) {
+    const int nvalid = tile_valid(a, it, vt);
     const int r = run0 + (lane & 7);
     const int j = (cached ? vt : vt - a.nct) * kTileK + r;
     if (!a.mode_b) {
@@ -282,13 +266,15 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       // it adds exactly nothing whatever its weight); absent keys get the id nobody sees.
       const int32_t* src = a.q_blk + it.q0;
       if (r < nvalid) {
-        if (cached) {
+        if (!cached) {
+          src = a.q_blk + it.q0 + j;
+        } else if (st.row0 >= 0) {
+          src = a.kv_blk + st.row0 + (lane & 7);
+        } else {
           int lp, slot;
           page_split(j, a.page_size, a.page_shift, &lp, &slot);
-          const int p = scalar_pages ? st.pw : st.krow;
+          const int p = a.page_table[(int64_t)it.s * a.max_pages + min(lp, a.max_pages - 1)];
           if (p >= 0 && p < a.num_pages) src = a.kv_blk + (int64_t)p * a.page_size + slot;
-        } else {
-          src = a.q_blk + it.q0 + j;
         }
       }
       if (lane < 8 && r >= nvalid) sm.kblk[sv][r] = kNoKeyBlk;
@@ -408,43 +394,42 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     // its cached tiles are staged in LDS first, so the tile loop reads its metadata from
     // LDS only and issues no memory loads but the tiles' own.
     const bool grp_pages = a.page_size % kRowsPerWave == 0;
-    const int win = grp_pages ? kWin : kWinRows;
-    for (int wb = ob; wb < oe; wb += win) {
-      const int nt = min(oe - wb, win);      // tiles in this window
+    const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
+    for (int wb = ob; wb < oe; wb += kWin) {
+      const int nt = min(oe - wb, kWin);     // tiles in this window
       __syncthreads();   // earlier readers of LDS (previous window or item) are finished
-      const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
-      for (int i = tid; i < nt; i += kThreads) sm.win_e[i] = list[wb + i];
-      if (grp_pages) {
-        for (int i = tid; i < nt * kWaves; i += kThreads) {
-          const int vt = list[wb + i / kWaves] >> 1, q = i % kWaves;
-          if (vt < a.nct) {
+      for (int i = tid; i < nt * kWaves; i += kThreads) {
+        const int ti = i / kWaves, q = i - ti * kWaves;
+        const int e = list[wb + ti];
+        if (q == 0) sm.win_e[ti] = e;
+        const int vt = e >> 1;
+        int row0 = -1;
+        if (vt < a.nct) {
+          const int j0 = vt * kTileK + kRowsPerWave * q;
+          if (grp_pages && j0 + kRowsPerWave <= it.kvl) {
             int lp, slot;
-            page_split(vt * kTileK + kRowsPerWave * q, a.page_size, a.page_shift, &lp, &slot);
-            sm.win_pg.grp[i / kWaves][q] = pt[min(lp, a.max_pages - 1)];
+            page_split(j0, a.page_size, a.page_shift, &lp, &slot);
+            const int p = pt[lp];
+            if (p >= 0 && p < a.num_pages) row0 = p * a.page_size + slot;
           }
+        } else {
+          const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q;
+          if (r0 + kRowsPerWave <= it.q_len) row0 = it.q0 + r0;
         }
-      } else {
-        for (int i = tid; i < nt * kTileK; i += kThreads) {
-          const int vt = list[wb + i / kTileK] >> 1, r = i % kTileK;
-          if (vt < a.nct) {
-            int lp, slot;
-            page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
-            sm.win_pg.row[i / kTileK][r] = pt[min(lp, a.max_pages - 1)];
-          }
-        }
+        sm.win_row[ti][q] = row0;
       }
       __syncthreads();
       auto entry = [&](int t) { return t < nt ? sm.win_e[t] : -1; };
 
       // Prologue: tiles 0 .. lead-1 issued; this wave waits for all of them but the last
       // (group A: tile 0; group B: tiles 0 and 1), then tile 0 is published.
-      Stage st;
       int issued = 0;
       for (int x = 0; x < lead; ++x) {
-        st = stage_lookup<HD, NI>(a, it, entry(x), x, sm);
+        const Stage st = meta_resolve(meta_read<HD>(x, nt, sm));
         issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo);
       }
-      st = stage_lookup<HD, NI>(a, it, entry(lead), lead, sm);
+      RawMeta raw = meta_read<HD>(lead, nt, sm);           // next tile to issue
+      int e_next = sm.win_e[0];                            // entry of the next tile to mask
       wait_vm(issued);
       __syncthreads();
       if (grp) __syncthreads();           // group B starts half a step later
@@ -503,17 +488,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         interleave<NM, NR, AHEAD>();
       };
 
-      // Vector phase of tile t: issue this wave's loads of tile t+lead and resolve the tile
-      // after it, then mask (partial tiles only) and the online softmax of S(t) into P(t),
-      // then wait until only the tile just issued is in flight.
+      // Vector phase of tile t: issue this wave's loads of tile t+lead and read the metadata
+      // of the tile after it, then mask (partial tiles only) and the online softmax of S(t)
+      // into P(t), then wait until only the tile just issued is in flight.
       auto vector_phase = [&](int t) {
         {
           const int x = t + lead;
-          issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo);
-          st = stage_lookup<HD, NI>(a, it, entry(x + 1), x + 1, sm);
+          issued = stage_fetch<HD, NI>(a, it, meta_resolve(raw), sm, x % kKStages, x % kVStages, fo);
+          raw = meta_read<HD>(x + 1, nt, sm);
         }
+        const int e_t = uni(e_next);
+        e_next = sm.win_e[min(t + 1, kWin - 1)];   // used next phase, only if t+1 < nt
         // Lane (col, hl) holds key 32kb + 8(v/4) + 4hl + v%4.
-        const int e_t = entry(t);
         const bool partial = e_t & 1;
         n_partial += partial;
         if (partial) {   // absent keys carry kNoKeyBlk, which no row sees
@@ -536,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = half_max(mx);
         const float mcand = mx * sl2;
         const bool grow = mcand > m + 8.f;
         if (__builtin_amdgcn_ballot_w64(grow)) {
