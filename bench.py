@@ -40,7 +40,74 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain copy kernel of known size")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs "
+                        "(FETCH_SIZE, then WRITE_SIZE) of `bench.py --calib-copy` into "
+                        "profiles/attn_traffic_C<config>.json and .md")
     return p.parse_args()
+
+
+CALIB_BYTES = 1 << 28        # the --calib-copy copy: 256 MiB read and 256 MiB written
+
+
+def summarize_traffic(args):
+    """HBM bytes per cold attention call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the 256 MiB calibration copy (an elementwise
+    multiply by one, 256 MiB in and 256 MiB out)."""
+    import csv
+    import numpy as np
+
+    def per_dispatch(path):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        return [rows[k] for k in sorted(rows)]
+
+    out = {}
+    for name, path in (("fetch", args.summarize_traffic[0]), ("write", args.summarize_traffic[1])):
+        d = per_dispatch(path)
+        copies = [v for k, v in d if "MulFunctor" in k]
+        calib = float(np.median(copies[-5:])) * 1024.0
+        factor = CALIB_BYTES / calib
+        calls, cur = [], None
+        for k, v in d:
+            if "attn_bf16_kernel" in k or "attn_f32_kernel" in k:
+                cur = [v]
+                calls.append(cur)
+            elif "combine_kernel" in k and cur is not None:
+                cur.append(v)
+        cold = calls[args.warmup:args.warmup + args.steps]
+        out[name] = {"calib_counter_bytes": calib, "factor": factor,
+                     "bytes_per_call": float(np.median([sum(c) for c in cold])) * 1024.0 * factor,
+                     "attn_kernel_bytes": float(np.median([c[0] for c in cold])) * 1024.0 * factor,
+                     "cold_calls": len(cold)}
+    rec = {"config": args.config, "kernel_hash": kernel_hash(),
+           "hbm_bytes_per_call": out["fetch"]["bytes_per_call"] + out["write"]["bytes_per_call"],
+           "fetch": out["fetch"], "write": out["write"],
+           "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o f -- python3 bench.py "
+                        f"--config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --calib-copy",
+                        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o w -- python3 bench.py "
+                        f"--config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --calib-copy",
+                        f"python3 bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
+                        f"--summarize-traffic <fetch csv> <write csv>"]}
+    base = os.path.join(ROOT, "profiles", f"attn_traffic_C{args.config}")
+    json.dump(rec, open(base + ".json", "w"), indent=1)
+    case_name = f"C{args.config}"
+    with open(base + ".md", "w") as f:
+        f.write(f"# HBM traffic of one cold attention call, {case_name}\n\n")
+        f.write("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), two separate rocprofv3 --pmc runs,\n")
+        f.write("each scaled by the same counter's reading for a 256 MiB device-to-device copy in the same run.\n\n")
+        for c in rec["commands"]:
+            f.write(f"    {c}\n")
+        f.write("\n| counter | calib copy (counter bytes) | factor | per call, scaled (bytes) | attention kernel only |\n")
+        f.write("|---|---|---|---|---|\n")
+        for name in ("fetch", "write"):
+            o = out[name]
+            f.write(f"| {name.upper()}_SIZE | {o['calib_counter_bytes']:.4g} | {o['factor']:.4f} | "
+                    f"{o['bytes_per_call']:.4g} | {o['attn_kernel_bytes']:.4g} |\n")
+        f.write(f"\nHBM bytes per call (fetch + write): {rec['hbm_bytes_per_call']:.4g}; kernel sources hash "
+                f"{rec['kernel_hash']} (bench.py reports it as roofline.traffic only while the hash matches).\n")
+    print(json.dumps(rec))
 
 
 def workload_stats(case):
@@ -118,6 +185,9 @@ def cpu_baseline(case, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence or kv head with no collective; see the design notes)",
@@ -194,10 +264,11 @@ def main():
     attn_warm_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in attn_warm]))
 
     if args.calib_copy:
-        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+        # A plain elementwise kernel (not the runtime's blit) that reads and writes 256 MiB.
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst_buf = torch.empty_like(src)
         for _ in range(5):
-            dst_buf.copy_(src)
+            torch.mul(src, 1.0, out=dst_buf)
         torch.cuda.synchronize()
 
     flops, cached_kv, live_kv, q_o = workload_stats(case)
