@@ -163,12 +163,13 @@ int device_cus() {
 }
 
 size_t plan_bytes_for(const bcp_meta* m, const Geo& g) {
-  return (size_t)plan_layout(m->batch, g.nqt, g.nkt).words * sizeof(int32_t);
+  return (size_t)plan_layout(m->batch, g.nqt, g.nkt, m->num_kv_heads).words * sizeof(int32_t);
 }
 
-// Partial results are needed only if some unit can have more than kMinChunk tiles.
+// Partial results are needed only if a (unit, kv head) pair can be cut by a range
+// boundary, i.e. if it can have more than one tile.
 size_t partial_bytes_for(const bcp_meta* m, const Geo& g) {
-  if (g.nkt <= kMinChunk) return 0;
+  if (g.nkt <= 1) return 0;
   return (size_t)kMaxPartialSlots * kRowsPerWG * (m->head_dim + 1) * sizeof(float);
 }
 
@@ -194,6 +195,7 @@ ClassifyArgs classify_args(const bcp_meta* m, const Geo& g) {
   a.mode_b = g.mode_b;
   a.phys_per_tile = std::max(1, g.tk / m->page_size);
   a.phys_tiles = g.nct;
+  a.num_kv_heads = m->num_kv_heads;
   return a;
 }
 
@@ -338,14 +340,13 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   a.max_pages = m->max_pages_per_seq;
   a.block_size = g.mode_b ? 1 : m->block_size;
   a.mode_b = g.mode_b;
-  a.max_items = plan_layout(m->batch, g.nqt, g.nkt).max_items;
+  a.max_items = plan_layout(m->batch, g.nqt, g.nkt, m->num_kv_heads).max_items;
   a.page_shift = (m->page_size & (m->page_size - 1)) ? -1 : __builtin_ctz((unsigned)m->page_size);
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)m->head_dim);
   a.scale_log2 = sc * 1.4426950408889634f;
 
   const int cus = device_cus();
-  const int64_t max_work = (int64_t)a.max_items * m->num_kv_heads;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_work, cus));
+  const int grid = kWGs;   // one workgroup per range of the plan
   hipError_t e = m->dtype == BCP_BF16 ? launch_attn_bf16(a, m->head_dim, grid, stream)
                                       : launch_attn_f32(a, m->head_dim, grid, stream);
   if (e != hipSuccess) return hip_fail(e, "launch attention");

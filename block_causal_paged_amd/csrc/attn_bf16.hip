@@ -8,10 +8,10 @@
 // whenever the max grows). Tiles the step plan marks as skipped are never loaded; only
 // partial tiles evaluate the mask.
 //
-// Work decomposition. A workgroup of 8 waves takes one work item: one kv head g, one
-// q-tile of a sequence (tile_q positions x the G query heads of g = 256 packed rows,
-// rho = position * G + head), and a contiguous chunk of that q-tile's non-skipped key
-// tiles. Wave w owns packed rows [32w, 32w+32), one 32-column MFMA block; two waves share
+// Work decomposition. A workgroup of 8 waves works through the items of its range of the
+// step plan; an item is one kv head g, one q-tile of a sequence (tile_q positions x the G
+// query heads of g = 256 packed rows, rho = position * G + head), and a contiguous run of
+// that q-tile's non-skipped key tiles. Wave w owns packed rows [32w, 32w+32), one 32-column MFMA block; two waves share
 // each SIMD, so one wave's matrix instructions overlap the other's softmax.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, wave64). Scores are computed
@@ -313,9 +313,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   const int grp = uni(wave) >> 2;   // 0: group A, 1: group B (scalar: guards barriers)
   const int lead = 2 + grp;         // tiles ahead of the current one that this wave issues
   const int G = a.G;
-  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
-  const int n_work = plan[0] * a.Hkv;
+  const int rg = range_of_wg(blockIdx.x);
+  const int w_begin = plan[L.wg + rg], w_end = plan[L.wg + rg + 1];
   const uint16_t* qg = (const uint16_t*)a.q;
   const float sl2 = a.scale_log2;
   // V transpose reads: lane (group g16 = lane/16, j = lane%16) is source lane 4*ta + tc of
@@ -351,12 +352,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   if (a.stats && blockIdx.x == 0 && tid == 0)   // skipped tiles of the whole grid, per kv head
     atomicAdd(&a.stats[2], (unsigned long long)a.Hkv * ((unsigned long long)L.units * a.nkt - plan[3]));
 
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int item = w / a.Hkv;
+  for (int item = w_begin; item < w_end; ++item) {
     Item it;
-    it.g = w - item * a.Hkv;
-    cint32* ip = plan + L.items + 4 * (int64_t)item;
-    const int u = ip[0], ob = ip[1], oe = ip[2], pslot = ip[3];
+    cint32* ip = plan + L.items + kItemWords * (int64_t)item;
+    const int u = ip[0], ob = ip[2], oe = ip[3], pslot = ip[4];
+    it.g = ip[1];
     it.s = u / a.nqt;
     const int r = u - it.s * a.nqt;
     live_rows(a.cu_q, it.s, a.total_q, a.max_q_len, &it.q0, &it.q_len);
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
           }
         if (hl == 0 && a.lse) a.lse[row] = lse2 * kLn2;
       } else {
-        const int64_t slot = (int64_t)pslot * a.Hkv + it.g;
+        const int64_t slot = pslot;
         float* pp = a.part_o + (slot * kRowsPerWG + rho) * HD;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)

@@ -21,17 +21,17 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int V4 = HD / 4;
   const int tid = threadIdx.x;
   const int G = a.G;
-  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
-  const int n_work = a.plan[0] * a.Hkv;
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
+  const int rg = range_of_wg(blockIdx.x);
+  const int w_begin = a.plan[L.wg + rg], w_end = a.plan[L.wg + rg + 1];
   const float* qg = (const float*)a.q;
   const float sl2 = a.scale_log2;
   if (a.stats && blockIdx.x == 0 && tid == 0)   // skipped tiles of the whole grid, per kv head
     atomicAdd(&a.stats[2], (unsigned long long)a.Hkv * ((unsigned long long)L.units * a.nkt - a.plan[3]));
 
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int item = w / a.Hkv, g = w - (w / a.Hkv) * a.Hkv;
-    const int* ip = a.plan + L.items + 4 * (int64_t)item;
-    const int u = ip[0], ob = ip[1], oe = ip[2], pslot = ip[3];
+  for (int item = w_begin; item < w_end; ++item) {
+    const int* ip = a.plan + L.items + kItemWords * (int64_t)item;
+    const int u = ip[0], g = ip[1], ob = ip[2], oe = ip[3], pslot = ip[4];
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
     int q0, q_len;
     live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         for (int d = 0; d < HD; d += 4) *(f32x4*)(op + d) = f32x4{ov[d] * inv, ov[d + 1] * inv, ov[d + 2] * inv, ov[d + 3] * inv};
         if (a.lse) a.lse[row] = lse2 * kLn2;
       } else {
-        const int64_t slot = (int64_t)pslot * a.Hkv + g;
+        const int64_t slot = pslot;
         float* pp = a.part_o + (slot * kRowsPerWG + rho) * HD;
 #pragma unroll
         for (int d = 0; d < HD; d += 4) *(f32x4*)(pp + d) = f32x4{ov[d] * inv, ov[d + 1] * inv, ov[d + 2] * inv, ov[d + 3] * inv};

@@ -15,44 +15,57 @@ namespace bcp {
 constexpr int kTileK = 64;
 constexpr int kRowsPerWG = 256;
 
-// Split-KV planning. A unit is one (sequence, q-tile); its non-skipped key tiles are cut
-// into nearly equal chunks so that the step has about kTargetWGs (chunk, kv head) work
-// items in total, each at least kMinChunk tiles long. Proof of the bounds used for buffer
-// sizes: with c >= max(kMinChunk, ceil(T*Hkv/kTargetWGs)) and T the non-skipped tile total
-// (the planner may lengthen c so that the items fit kTargetWGs exactly),
-// sum_u ceil(cnt_u/c) <= T/c + U <= kTargetWGs/Hkv + U items; a split unit has cnt_u > c,
-// so its ceil(cnt_u/c) < 2*cnt_u/c and all split items times Hkv stay below 2*kTargetWGs.
-constexpr int kTargetWGs = 256;
+// Split-KV planning. The work of a step is the sequence of (kv head, unit, key tile)
+// visits, ordered by kv head, then unit, then tile (a unit is one (sequence, q-tile); its
+// key tiles are the non-skipped ones). It is cut into at most kWGs near-equal contiguous
+// ranges, each at least kMinChunk visits long when the step has that much work. Range r
+// runs on workgroup (r % kPerXcd) * kXcds + r / kPerXcd: workgroups are dealt to the XCDs
+// in turn, so each XCD gets kPerXcd consecutive ranges, mostly of one kv head, whose keys
+// and values then stay in that XCD's L2 across the q-tiles that reuse them.
+// A range holds whole (unit, head) pairs plus at most one piece at each end; a pair cut by
+// range boundaries is computed in pieces, each writing a normalized partial result that
+// the combine kernel merges. There are fewer than kWGs boundaries and each lies inside at
+// most one pair, so fewer than kWGs pairs are split and they have fewer than 2*kWGs pieces.
+constexpr int kWGs = 256;
+constexpr int kXcds = 8;
+constexpr int kPerXcd = kWGs / kXcds;
 constexpr int kMinChunk = 4;
-constexpr int kMaxPartialSlots = 2 * kTargetWGs;
+constexpr int kMaxPartialSlots = 2 * kWGs;
 
 constexpr int kNegInfBlk = INT32_MIN;   // a committed row in mode A: seen by every live row
 constexpr int kNoKeyBlk = INT32_MAX;    // an absent key: seen by nobody
 
 // Step plan, in int32 words:
-//   [0, 8)                header: n_items, n_split_units, chunk, total tiles, tile_q, tile_k,
-//                         nqt, nkt
-//   cnt   [U]             non-skipped key tiles per unit (U = batch * nqt)
-//   list  [U * nkt]       per unit, its non-skipped virtual tile indices in order, each
-//                         stored as (t << 1) | is_partial; t < nct is cached tile t,
-//                         t >= nct is live tile t - nct
-//   items [max_items][4]  unit, first ordinal, end ordinal, partial slot (-1: unit not split)
-//   split [U][4]          unit, first partial slot, number of splits, 0
+//   [0, 8)                  header: n_items, n_split, workgroups used, total tiles T, tile_q,
+//                           tile_k, nqt, nkt
+//   cnt   [U]               non-skipped key tiles per unit (U = batch * nqt)
+//   list  [U * nkt]         per unit, its non-skipped virtual tile indices in order, each
+//                           stored as (t << 1) | is_partial; t < nct is cached tile t,
+//                           t >= nct is live tile t - nct
+//   upre  [U + 1]           exclusive prefix sums of cnt (upre[U] = T)
+//   wg    [kWGs + 1]        first item of each range; wg[kWGs] = n_items
+//   items [max_items][8]    unit, kv head, first ordinal, end ordinal, partial slot (-1 when
+//                           the item is a whole pair), 0, 0, 0
+//   split [kWGs][4]         unit, kv head, first partial slot, number of pieces
+constexpr int kItemWords = 8;
+
 struct PlanLayout {
-  int64_t cnt, list, items, split, words;
+  int64_t cnt, list, upre, wg, items, split, words;
   int units, nkt, max_items;
 };
 
-__host__ __device__ inline PlanLayout plan_layout(int batch, int nqt, int nkt) {
+__host__ __device__ inline PlanLayout plan_layout(int batch, int nqt, int nkt, int hkv) {
   PlanLayout p;
   p.units = batch * nqt;
   p.nkt = nkt;
-  p.max_items = p.units + kTargetWGs;
+  p.max_items = p.units * hkv + kWGs;
   p.cnt = 8;
   p.list = p.cnt + p.units;
-  p.items = p.list + (int64_t)p.units * nkt;
-  p.split = p.items + 4 * (int64_t)p.max_items;
-  p.words = p.split + 4 * (int64_t)p.units;
+  p.upre = p.list + (int64_t)p.units * nkt;
+  p.wg = p.upre + p.units + 1;
+  p.items = p.wg + kWGs + 1;
+  p.split = p.items + kItemWords * (int64_t)p.max_items;
+  p.words = p.split + 4 * (int64_t)kWGs;
   return p;
 }
 
@@ -66,7 +79,7 @@ struct ClassifyArgs {
   int32_t* phys_page;     // may be null
   int32_t* plan;          // may be null
   int batch, total_q, tile_q, tile_k, nqt, nct, nkt, block_size, page_size, num_pages,
-      max_pages, max_q_len, mode_b, phys_per_tile, phys_tiles;
+      max_pages, max_q_len, mode_b, phys_per_tile, phys_tiles, num_kv_heads;
   int grid_q;             // q-tile workgroups per sequence: max(nqt, 1)
 };
 
@@ -84,7 +97,7 @@ struct AttnArgs {
   void* out;
   float* lse;
   float* part_o;          // [kMaxPartialSlots][256][d] normalized partial outputs
-  float* part_lse;        // [kMaxPartialSlots][256] log2-domain partial LSE
+  float* part_lse;        // [kMaxPartialSlots][256] log2-domain partial LSE (slot = piece)
   const int32_t* cu_q;
   const int32_t* kv_len;
   const int32_t* page_table;
@@ -121,6 +134,9 @@ hipError_t launch_combine(const AttnArgs& a, int head_dim, int is_bf16, int grid
 hipError_t launch_commit(const CommitArgs& a, int grid, hipStream_t stream);
 
 // ----------------------------------------------------------------------------------------
+// Range of the step plan that workgroup `wg` works through (see the split-KV planning).
+__host__ __device__ inline int range_of_wg(int wg) { return (wg % kXcds) * kPerXcd + wg / kXcds; }
+
 // Device helpers shared by the kernels.
 // ----------------------------------------------------------------------------------------
 #ifdef __HIPCC__

@@ -21,15 +21,14 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   constexpr int RPW = 256 / V4;           // rows per work item (one row per V4 threads)
   constexpr int NGRP = kRowsPerWG / RPW;  // row groups per (split unit, kv head)
   constexpr int MAXC = 8;                 // splits merged per pass, loads issued together
-  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
-  const int n_work = plan[1] * a.Hkv * NGRP;
+  const int n_work = plan[1] * NGRP;
   const int tid = threadIdx.x, d4 = tid % V4, rr = tid / V4;
   for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int grp = w % NGRP, eg = w / NGRP;
-    const int e = eg / a.Hkv, g = eg - (eg / a.Hkv) * a.Hkv;
+    const int grp = w % NGRP, e = w / NGRP;
     cint32* sp = plan + L.split + 4 * (int64_t)e;
-    const int u = sp[0], ps0 = sp[1], n = sp[2];
+    const int u = sp[0], g = sp[1], ps0 = sp[2], n = sp[3];
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
     int q0, q_len;
     live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
@@ -40,7 +39,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     // all their loads in flight together.
     float M = -INFINITY;
     for (int c = 0; c < n; ++c)
-      M = fmaxf(M, a.part_lse[((int64_t)(ps0 + c) * a.Hkv + g) * kRowsPerWG + rho]);
+      M = fmaxf(M, a.part_lse[(int64_t)(ps0 + c) * kRowsPerWG + rho]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (M != -INFINITY) {
@@ -50,7 +49,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
           const int c = min(c0 + k, n - 1);
-          const int64_t slot = (int64_t)(ps0 + c) * a.Hkv + g;
+          const int64_t slot = ps0 + c;
           lc[k] = a.part_lse[slot * kRowsPerWG + rho];
           oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
         }

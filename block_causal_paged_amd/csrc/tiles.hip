@@ -49,20 +49,6 @@ __device__ int block_scan_excl(int v, int* lds16, int* total) {
   return before + x - v;
 }
 
-// Maximum of v over the workgroup (every thread gets it).
-__device__ int block_max(int v, int* lds16) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-  if (lane == 0) lds16[wave] = x;
-  __syncthreads();
-  int all = lds16[0];
-  for (int w = 1; w < nw; ++w) all = max(all, lds16[w]);
-  __syncthreads();
-  return all;
-}
-
 __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
   __shared__ int red[2][4];
   __shared__ int scan_lds[16];
@@ -101,7 +87,7 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
   }
 
   const int64_t list_base = (int64_t)u * a.nkt;
-  PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
+  PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.num_kv_heads);
   int running = 0;
   for (int base = 0; has_tiles && base < a.nkt; base += blockDim.x) {
     const int t = base + tid;
@@ -167,82 +153,181 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
   }
 }
 
-// One workgroup turns the per-unit tile counts into balanced (unit, chunk) work items.
-__global__ __launch_bounds__(1024) void planner_kernel(PlanArgs a) {
-  __shared__ int scan_lds[16];
-  int* plan = a.plan;
-  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt);
-  const int units = L.units;
-  const int tid = threadIdx.x;
-
-  // Total non-skipped tiles.
-  int part = 0;
-  for (int u = tid; u < units; u += blockDim.x) part += plan[L.cnt + u];
-  int total_tiles;
-  block_scan_excl(part, scan_lds, &total_tiles);
-
-  const long long work = (long long)total_tiles * a.num_kv_heads;
-  int chunk = (int)((work + kTargetWGs - 1) / kTargetWGs);
-  chunk = max(chunk, kMinChunk);
-  // Rounding each unit up to whole chunks can leave slightly more than kTargetWGs work
-  // items, and the few left over would run as a second round after everything else. Take
-  // the smallest chunk length that keeps the item count within kTargetWGs when one exists
-  // (the count only falls as the chunk grows, so a bisection finds it).
-  {
-    int mx = 0;
-    for (int u = tid; u < units; u += blockDim.x) mx = max(mx, plan[L.cnt + u]);
-    const int cmax = block_max(mx, scan_lds);
-    auto fits = [&](int c) {
-      int p = 0, tot;
-      for (int u = tid; u < units; u += blockDim.x) p += (plan[L.cnt + u] + c - 1) / c;
-      block_scan_excl(p, scan_lds, &tot);
-      return (long long)tot * a.num_kv_heads <= kTargetWGs;
-    };
-    if (cmax > chunk && !fits(chunk) && fits(cmax)) {
-      int lo = chunk, hi = cmax;   // fits(lo) is false, fits(hi) is true
-      while (hi - lo > 1) {
-        const int mid = lo + (hi - lo) / 2;
-        if (fits(mid)) hi = mid;
-        else lo = mid;
-      }
-      chunk = hi;
+// Exclusive prefix sums of three values at once over a workgroup of kPlanThreads.
+constexpr int kPlanThreads = 256;
+constexpr int kPlanLdsUnits = 4096;
+struct Int3 {
+  int x, y, z;
+};
+__device__ Int3 block_scan3_excl(Int3 v, Int3* lds, Int3* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Int3 s = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(s.x, o), b = __shfl_up(s.y, o), c = __shfl_up(s.z, o);
+    if (lane >= o) {
+      s.x += a;
+      s.y += b;
+      s.z += c;
     }
   }
-
-  int item_carry = 0, slot_carry = 0, split_carry = 0;
-  for (int base = 0; base < units; base += blockDim.x) {
-    const int u = base + tid;
-    const int cnt = u < units ? plan[L.cnt + u] : 0;
-    const int nch = (cnt + chunk - 1) / chunk;
-    const bool split = nch > 1;
-    int t_items, t_slots, t_split;
-    const int item0 = item_carry + block_scan_excl(nch, scan_lds, &t_items);
-    const int slot0 = slot_carry + block_scan_excl(split ? nch : 0, scan_lds, &t_slots);
-    const int sidx = split_carry + block_scan_excl(split ? 1 : 0, scan_lds, &t_split);
-    if (u < units) {
-      for (int k = 0; k < nch; ++k) {
-        int* it = plan + L.items + 4 * (int64_t)(item0 + k);
-        it[0] = u;
-        it[1] = (int)(((long long)k * cnt) / nch);
-        it[2] = (int)(((long long)(k + 1) * cnt) / nch);
-        it[3] = split ? slot0 + k : -1;
-      }
-      if (split) {
-        int* sp = plan + L.split + 4 * (int64_t)sidx;
-        sp[0] = u;
-        sp[1] = slot0;
-        sp[2] = nch;
-        sp[3] = 0;
-      }
+  if (lane == 63) lds[wave] = s;
+  __syncthreads();
+  Int3 before = {0, 0, 0}, all = {0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const Int3 t = lds[w];
+    if (w < wave) {
+      before.x += t.x;
+      before.y += t.y;
+      before.z += t.z;
     }
-    item_carry += t_items;
-    slot_carry += t_slots;
-    split_carry += t_split;
+    all.x += t.x;
+    all.y += t.y;
+    all.z += t.z;
+  }
+  __syncthreads();
+  *total = all;
+  return Int3{before.x + s.x - v.x, before.y + s.y - v.y, before.z + s.z - v.z};
+}
+
+// One workgroup turns the per-unit tile counts into the ranges of the step's visits and
+// the items (whole or partial (unit, kv head) pairs) that make them up. Each thread takes
+// a contiguous run of units, then of pairs, so one scan orders everything.
+__global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
+  __shared__ Int3 scan_lds[kPlanThreads / 64];
+  __shared__ int wg_first[kWGs + 1];
+  __shared__ int s_cnt[kPlanLdsUnits], s_upre[kPlanLdsUnits];
+  int* plan = a.plan;
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.num_kv_heads);
+  const int units = L.units, hkv = a.num_kv_heads;
+  const int tid = threadIdx.x;
+  // Per-unit counts and their prefix sums live in LDS when they fit (else in the plan).
+  const bool in_lds = units <= kPlanLdsUnits;
+  if (in_lds)
+    for (int u = tid; u < units; u += kPlanThreads) s_cnt[u] = plan[L.cnt + u];
+  __syncthreads();
+  auto cnt_of = [&](int u) { return in_lds ? s_cnt[u] : plan[L.cnt + u]; };
+
+  // Prefix sums of the per-unit tile counts.
+  const int upt = (units + kPlanThreads - 1) / kPlanThreads;
+  const int u0 = min(units, tid * upt), u1 = min(units, u0 + upt);
+  int mine = 0;
+  for (int u = u0; u < u1; ++u) mine += cnt_of(u);
+  Int3 tot;
+  int run = block_scan3_excl(Int3{mine, 0, 0}, scan_lds, &tot).x;
+  for (int u = u0; u < u1; ++u) {
+    plan[L.upre + u] = run;
+    if (in_lds) s_upre[u] = run;
+    run += cnt_of(u);
+  }
+  const int total_tiles = tot.x;
+  if (tid == 0) plan[L.upre + units] = total_tiles;
+  for (int w = tid; w <= kWGs; w += kPlanThreads) wg_first[w] = INT32_MAX;
+  __syncthreads();   // upre is read back below by other threads
+  auto upre_of = [&](int u) { return in_lds ? s_upre[u] : plan[L.upre + u]; };
+
+  // Range r covers visits [b(r), b(r+1)) of W = T * Hkv, for n_wg <= kWGs ranges: the
+  // first `rem` ranges have q + 1 visits, the others q. (32-bit: the plan supports steps of
+  // fewer than 2^31 visits.)
+  const unsigned W = (unsigned)total_tiles * (unsigned)hkv;
+  const unsigned n_wg = max(1u, min((unsigned)kWGs, W / kMinChunk));
+  const unsigned q = W / n_wg, rem = W - q * n_wg, big = rem * (q + 1);
+  auto b = [&](unsigned r) { return r * q + min(r, rem); };
+  auto range_of = [&](unsigned x) { return x < big ? x / (q + 1) : rem + (x - big) / q; };
+  // Pair pr = (kv head g, unit u), head-major: its visits start at S = g*T + upre[u].
+  auto pair_info = [&](int pr, int* u, int* g, int* cnt, unsigned* S, unsigned* rf) {
+    *g = pr / units;
+    *u = pr - *g * units;
+    *cnt = cnt_of(*u);
+    *S = (unsigned)*g * (unsigned)total_tiles + (unsigned)upre_of(*u);
+    *rf = *cnt > 0 ? range_of(*S) : 0;
+    return *cnt > 0 ? (int)(range_of(*S + *cnt - 1) - *rf) + 1 : 0;   // pieces
+  };
+
+  const int pairs = units * hkv;
+  const int ppt = (pairs + kPlanThreads - 1) / kPlanThreads;
+  const int p0 = min(pairs, tid * ppt), p1 = min(pairs, p0 + ppt);
+  Int3 own = {0, 0, 0};   // items, partial slots, split pairs of this thread's pairs
+  for (int pr = p0; pr < p1; ++pr) {
+    int u, g, cnt;
+    unsigned S, rf;
+    const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+    own.x += n;
+    own.y += n > 1 ? n : 0;
+    own.z += n > 1 ? 1 : 0;
+  }
+  Int3 all;
+  Int3 at = block_scan3_excl(own, scan_lds, &all);
+  for (int pr = p0; pr < p1; ++pr) {
+    int u, g, cnt;
+    unsigned S, rf;
+    const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+    const bool split = n > 1;
+    for (int k = 0; k < n; ++k) {
+      const unsigned r = rf + k;
+      const unsigned lo = max(b(r), S), hi = min(b(r + 1), S + cnt);
+      int* it = plan + L.items + kItemWords * (int64_t)(at.x + k);
+      it[0] = u;
+      it[1] = g;
+      it[2] = (int)(lo - S);
+      it[3] = (int)(hi - S);
+      it[4] = split ? at.y + k : -1;
+      it[5] = 0;
+      it[6] = 0;
+      it[7] = 0;
+      if (lo == b(r)) wg_first[r] = at.x + k;   // the piece that opens range r
+    }
+    if (split) {
+      int* sp = plan + L.split + 4 * (int64_t)at.z;
+      sp[0] = u;
+      sp[1] = g;
+      sp[2] = at.y;
+      sp[3] = n;
+    }
+    at.x += n;
+    at.y += split ? n : 0;
+    at.z += split ? 1 : 0;
+  }
+  if (tid == 0) wg_first[kWGs] = all.x;
+  __syncthreads();
+  // A range that opens no item (an empty one, or one past n_wg) starts where the next
+  // range does: the suffix minimum over the opened starts (which increase with r).
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    constexpr int PER = (kWGs + 1 + kPlanThreads - 1) / kPlanThreads;   // entries per thread
+    int v[PER];
+    int m = INT32_MAX;
+#pragma unroll
+    for (int k = PER - 1; k >= 0; --k) {
+      const int w = tid * PER + k;
+      v[k] = w <= kWGs ? wg_first[w] : INT32_MAX;
+      m = min(m, v[k]);
+      v[k] = m;   // suffix min inside this thread's entries
+    }
+    // Suffix min across threads: min over the entries of later threads.
+    int x = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_down(x, o);
+      if (lane + o < 64) x = min(x, y);
+    }
+    __shared__ int wave_min[kPlanThreads / 64];
+    if (lane == 0) wave_min[wave] = x;
+    __syncthreads();
+    int later = __shfl_down(x, 1);
+    if (lane == 63) later = INT32_MAX;
+    for (int w = wave + 1; w < kPlanThreads / 64; ++w) later = min(later, wave_min[w]);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int w = tid * PER + k;
+      if (w <= kWGs) plan[L.wg + w] = min(v[k], later);
+    }
   }
   if (tid == 0) {
-    plan[0] = item_carry;
-    plan[1] = split_carry;
-    plan[2] = chunk;
+    plan[0] = all.x;
+    plan[1] = all.z;
+    plan[2] = n_wg;
     plan[3] = total_tiles;
     plan[4] = a.tile_q;
     plan[5] = a.tile_k;
@@ -259,7 +344,7 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_planner(const PlanArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
   return hipGetLastError();
 }
 

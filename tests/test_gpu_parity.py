@@ -293,6 +293,72 @@ def test_tile_classes_workloads(workloads, n):
         assert (got == bcp.BCP_TILE_FULL).sum() == 4 * 8256 and (got == bcp.BCP_TILE_PARTIAL).sum() == 0
 
 
+# Step-plan invariants. The plan is the library's internal work list (layout documented in
+# its internal header, mirrored here): the (unit, kv head, key tile) visits are cut into
+# contiguous ranges of near-equal length, one per workgroup; every pair's tiles are covered
+# exactly once, in order; pieces of a cut pair own distinct partial slots.
+N_WGS, ITEM_WORDS, MAX_SLOTS = 256, 8, 512
+
+
+def _plan_words(case, dc):
+    meta = bcp.StepMeta(**dc.meta_kwargs())
+    plan_t = torch.zeros(bcp.plan_size(meta), dtype=torch.uint8, device="cuda")
+    bcp.build_tile_mask(meta, plan=plan_t)
+    torch.cuda.synchronize()
+    return plan_t.view(torch.int32).cpu().numpy(), bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
+
+
+@pytest.mark.parametrize("n", [2, 4, 5, 3])
+def test_plan_ranges_cover_every_visit_once(workloads, n):
+    case = workloads(n)
+    w, nqt, nkt = _plan_words(case, DeviceCase(case))
+    U, hkv = case.batch * nqt, case.num_kv_heads
+    cnt_off = 8
+    list_off = cnt_off + U
+    upre_off = list_off + U * nkt
+    wg_off = upre_off + U + 1
+    items_off = wg_off + N_WGS + 1
+    max_items = U * hkv + N_WGS
+    split_off = items_off + ITEM_WORDS * max_items
+    n_items, n_split, n_wg, total = int(w[0]), int(w[1]), int(w[2]), int(w[3])
+    cnt = w[cnt_off:cnt_off + U].astype(np.int64)
+    assert total == cnt.sum()
+    # The tile counts agree with the oracle's classes (non-skipped tiles per unit).
+    cls = oracle_tiles(case, 256 // (case.num_q_heads // hkv), 64)
+    np.testing.assert_array_equal(cnt, (cls != 0).reshape(U, -1).sum(axis=1))
+    wg = w[wg_off:wg_off + N_WGS + 1]
+    assert wg[0] == 0 and wg[-1] == n_items and np.all(np.diff(wg) >= 0)
+    items = w[items_off:items_off + ITEM_WORDS * n_items].reshape(n_items, ITEM_WORDS)
+    covered = {}
+    loads = np.zeros(N_WGS, dtype=np.int64)
+    slots = []
+    for k in range(N_WGS):
+        for it in items[wg[k]:wg[k + 1]]:
+            u, g, ob, oe, ps = (int(x) for x in it[:5])
+            assert 0 <= u < U and 0 <= g < hkv and 0 <= ob < oe <= cnt[u]
+            covered.setdefault((u, g), []).append((ob, oe, ps))
+            loads[k] += oe - ob
+            if ps >= 0:
+                slots.append(ps)
+    for u in range(U):
+        for g in range(hkv):
+            pieces = covered.get((u, g), [])
+            if cnt[u] == 0:
+                assert not pieces
+                continue
+            assert pieces[0][0] == 0 and pieces[-1][1] == cnt[u]
+            assert all(a[1] == b[0] for a, b in zip(pieces, pieces[1:]))
+            assert (len(pieces) == 1) == (pieces[0][2] < 0)
+    assert len(slots) == len(set(slots)) and (not slots or max(slots) < MAX_SLOTS)
+    splits = w[split_off:split_off + 4 * n_split].reshape(n_split, 4)
+    for u, g, ps0, npieces in splits:
+        assert [p[2] for p in covered[(int(u), int(g))]] == list(range(ps0, ps0 + npieces))
+    # Balance: ranges differ by at most one visit.
+    used = loads[:n_wg]
+    assert used.max() - used.min() <= 1 and loads[n_wg:].sum() == 0
+    assert used.sum() == total * hkv
+
+
 def test_stats_count_tiles(workloads):
     case = workloads(4)
     dc = DeviceCase(case)
