@@ -49,6 +49,20 @@ __device__ int block_scan_excl(int v, int* lds16, int* total) {
   return before + x - v;
 }
 
+// Maximum over the workgroup (every thread gets it); lds holds one int per wave.
+__device__ int block_max(int v, int* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max(v);
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  int m = lds[0];
+  for (int w = 1; w < nw; ++w) m = max(m, lds[w]);
+  __syncthreads();
+  return m;
+}
+
+constexpr int kClsLdsTiles = 2048;   // key tiles whose mode-B block-id ranges fit in LDS
+
 __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
   __shared__ int red[2][4];
   __shared__ int scan_lds[16];
@@ -86,6 +100,37 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
     }
   }
 
+  // Mode B: block-id range of every key tile, computed cooperatively (one wave per tile,
+  // one lane per key) into LDS when the grid fits; each thread then classifies its tiles.
+  __shared__ int s_kmin[kClsLdsTiles], s_kmax[kClsLdsTiles];
+  const bool coop = a.mode_b && has_tiles && nrows > 0 && a.nkt <= kClsLdsTiles;
+  if (coop) {
+    for (int t = wave; t < a.nkt; t += blockDim.x / 64) {
+      int mn = INT32_MAX, mx = INT32_MIN;
+      const bool cached = t < a.nct;
+      const int lo = (cached ? t : t - a.nct) * a.tile_k;
+      const int nvalid = clampi((cached ? kvl : q_len) - lo, 0, a.tile_k);
+      for (int j = lo + lane; j < lo + nvalid; j += 64) {
+        int b;
+        if (cached) {
+          const int p = translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages);
+          b = p < 0 ? kNoKeyBlk : a.kv_blk[(int64_t)p * a.page_size + (j % a.page_size)];
+        } else {
+          b = a.q_blk[q0 + j];
+        }
+        mn = min(mn, b);
+        mx = max(mx, b);
+      }
+      mn = wave_min(mn);
+      mx = wave_max(mx);
+      if (lane == 0) {
+        s_kmin[t] = mn;
+        s_kmax[t] = mx;
+      }
+    }
+    __syncthreads();
+  }
+
   const int64_t list_base = (int64_t)u * a.nkt;
   PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.num_kv_heads);
   int running = 0;
@@ -99,6 +144,9 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
         nvalid = clampi(kvl - lo, 0, a.tile_k);
         if (!a.mode_b) {
           kmin = kmax = kNegInfBlk;
+        } else if (coop) {
+          kmin = s_kmin[t];
+          kmax = s_kmax[t];
         } else {
           kmin = INT32_MAX;
           kmax = INT32_MIN;
@@ -115,6 +163,9 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
         if (!a.mode_b) {
           kmin = lo / a.block_size;
           kmax = (lo + max(nvalid, 1) - 1) / a.block_size;
+        } else if (coop) {
+          kmin = s_kmin[t];
+          kmax = s_kmax[t];
         } else {
           kmin = INT32_MAX;
           kmax = INT32_MIN;
@@ -227,56 +278,48 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
   __syncthreads();   // upre is read back below by other threads
   auto upre_of = [&](int u) { return in_lds ? s_upre[u] : plan[L.upre + u]; };
 
-  // Range r covers visits [b(r), b(r+1)) of W = T * Hkv, for n_wg <= kWGs ranges: the
-  // first `rem` ranges have q + 1 visits, the others q. (32-bit: the plan supports steps of
-  // fewer than 2^31 visits.)
   const unsigned W = (unsigned)total_tiles * (unsigned)hkv;
-  const unsigned n_wg = max(1u, min((unsigned)kWGs, W / kMinChunk));
-  const unsigned q = W / n_wg, rem = W - q * n_wg, big = rem * (q + 1);
-  auto b = [&](unsigned r) { return r * q + min(r, rem); };
-  auto range_of = [&](unsigned x) { return x < big ? x / (q + 1) : rem + (x - big) / q; };
-  // Pair pr = (kv head g, unit u), head-major: its visits start at S = g*T + upre[u].
-  auto pair_info = [&](int pr, int* u, int* g, int* cnt, unsigned* S, unsigned* rf) {
-    *g = pr / units;
-    *u = pr - *g * units;
-    *cnt = cnt_of(*u);
-    *S = (unsigned)*g * (unsigned)total_tiles + (unsigned)upre_of(*u);
-    *rf = *cnt > 0 ? range_of(*S) : 0;
-    return *cnt > 0 ? (int)(range_of(*S + *cnt - 1) - *rf) + 1 : 0;   // pieces
-  };
-
   const int pairs = units * hkv;
-  const int ppt = (pairs + kPlanThreads - 1) / kPlanThreads;
-  const int p0 = min(pairs, tid * ppt), p1 = min(pairs, p0 + ppt);
-  Int3 own = {0, 0, 0};   // items, partial slots, split pairs of this thread's pairs
-  for (int pr = p0; pr < p1; ++pr) {
-    int u, g, cnt;
-    unsigned S, rf;
-    const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
-    own.x += n;
-    own.y += n > 1 ? n : 0;
-    own.z += n > 1 ? 1 : 0;
-  }
+  unsigned n_wg;
   Int3 all;
-  Int3 at = block_scan3_excl(own, scan_lds, &all);
-  for (int pr = p0; pr < p1; ++pr) {
-    int u, g, cnt;
-    unsigned S, rf;
-    const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+  if (pairs <= kPlanThreads) {
+    // Few (unit, kv head) pairs (decode batches): cut each pair into ceil(cnt/c) near-equal
+    // chunks, one range each, with the smallest chunk length c >= max(kMinChunk,
+    // ceil(W/kWGs)) that keeps the chunk count within kWGs (the count only falls as c
+    // grows, so a bisection finds it). One item per range, at most c visits long.
+    const int pr = tid;
+    const int u = pr < pairs ? pr % units : 0, g = pr < pairs ? pr / units : 0;
+    const int cnt = pr < pairs ? cnt_of(u) : 0;
+    Int3 t3;
+    auto chunks = [&](int c) {
+      block_scan3_excl(Int3{(cnt + c - 1) / c, 0, 0}, scan_lds, &t3);
+      return t3.x;
+    };
+    const int cmax = block_max(cnt, (int*)scan_lds);
+    int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
+    if (cmax > c && chunks(c) > kWGs) {
+      int lo = c, hi = cmax;   // too many chunks at lo; one per pair (<= kWGs) at hi
+      while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (chunks(mid) <= kWGs) hi = mid;
+        else lo = mid;
+      }
+      c = hi;
+    }
+    const int n = cnt > 0 ? (cnt + c - 1) / c : 0;
     const bool split = n > 1;
+    const Int3 at = block_scan3_excl(Int3{n, split ? n : 0, split ? 1 : 0}, scan_lds, &all);
     for (int k = 0; k < n; ++k) {
-      const unsigned r = rf + k;
-      const unsigned lo = max(b(r), S), hi = min(b(r + 1), S + cnt);
       int* it = plan + L.items + kItemWords * (int64_t)(at.x + k);
       it[0] = u;
       it[1] = g;
-      it[2] = (int)(lo - S);
-      it[3] = (int)(hi - S);
+      it[2] = (int)(((long long)k * cnt) / n);
+      it[3] = (int)(((long long)(k + 1) * cnt) / n);
       it[4] = split ? at.y + k : -1;
       it[5] = 0;
       it[6] = 0;
       it[7] = 0;
-      if (lo == b(r)) wg_first[r] = at.x + k;   // the piece that opens range r
+      wg_first[at.x + k] = at.x + k;
     }
     if (split) {
       int* sp = plan + L.split + 4 * (int64_t)at.z;
@@ -285,9 +328,67 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
       sp[2] = at.y;
       sp[3] = n;
     }
-    at.x += n;
-    at.y += split ? n : 0;
-    at.z += split ? 1 : 0;
+    n_wg = max(1, all.x);
+  } else {
+    // Range r covers visits [b(r), b(r+1)) of W = T * Hkv, for n_wg <= kWGs ranges: the
+    // first `rem` ranges have q + 1 visits, the others q. (32-bit: the plan supports steps of
+    // fewer than 2^31 visits.)
+    n_wg = max(1u, min((unsigned)kWGs, W / kMinChunk));
+    const unsigned q = W / n_wg, rem = W - q * n_wg, big = rem * (q + 1);
+    auto b = [&](unsigned r) { return r * q + min(r, rem); };
+    auto range_of = [&](unsigned x) { return x < big ? x / (q + 1) : rem + (x - big) / q; };
+    // Pair pr = (kv head g, unit u), head-major: its visits start at S = g*T + upre[u].
+    auto pair_info = [&](int pr, int* u, int* g, int* cnt, unsigned* S, unsigned* rf) {
+      *g = pr / units;
+      *u = pr - *g * units;
+      *cnt = cnt_of(*u);
+      *S = (unsigned)*g * (unsigned)total_tiles + (unsigned)upre_of(*u);
+      *rf = *cnt > 0 ? range_of(*S) : 0;
+      return *cnt > 0 ? (int)(range_of(*S + *cnt - 1) - *rf) + 1 : 0;   // pieces
+    };
+
+    const int ppt = (pairs + kPlanThreads - 1) / kPlanThreads;
+    const int p0 = min(pairs, tid * ppt), p1 = min(pairs, p0 + ppt);
+    Int3 own = {0, 0, 0};   // items, partial slots, split pairs of this thread's pairs
+    for (int pr = p0; pr < p1; ++pr) {
+      int u, g, cnt;
+      unsigned S, rf;
+      const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+      own.x += n;
+      own.y += n > 1 ? n : 0;
+      own.z += n > 1 ? 1 : 0;
+    }
+    Int3 at = block_scan3_excl(own, scan_lds, &all);
+    for (int pr = p0; pr < p1; ++pr) {
+      int u, g, cnt;
+      unsigned S, rf;
+      const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+      const bool split = n > 1;
+      for (int k = 0; k < n; ++k) {
+        const unsigned r = rf + k;
+        const unsigned lo = max(b(r), S), hi = min(b(r + 1), S + cnt);
+        int* it = plan + L.items + kItemWords * (int64_t)(at.x + k);
+        it[0] = u;
+        it[1] = g;
+        it[2] = (int)(lo - S);
+        it[3] = (int)(hi - S);
+        it[4] = split ? at.y + k : -1;
+        it[5] = 0;
+        it[6] = 0;
+        it[7] = 0;
+        if (lo == b(r)) wg_first[r] = at.x + k;   // the piece that opens range r
+      }
+      if (split) {
+        int* sp = plan + L.split + 4 * (int64_t)at.z;
+        sp[0] = u;
+        sp[1] = g;
+        sp[2] = at.y;
+        sp[3] = n;
+      }
+      at.x += n;
+      at.y += split ? n : 0;
+      at.z += split ? 1 : 0;
+    }
   }
   if (tid == 0) wg_first[kWGs] = all.x;
   __syncthreads();
