@@ -11,8 +11,10 @@
 // Work decomposition. A workgroup of 8 waves works through the items of its range of the
 // step plan; an item is one kv head g, one q-tile of a sequence (tile_q positions x the G
 // query heads of g = 256 packed rows, rho = position * G + head), and a contiguous run of
-// that q-tile's non-skipped key tiles. Wave w owns packed rows [32w, 32w+32), one 32-column MFMA block; two waves share
-// each SIMD, so one wave's matrix instructions overlap the other's softmax.
+// that q-tile's non-skipped key tiles. Wave w owns packed rows [32w, 32w+32), one
+// 32-column MFMA block. Waves 0-3 and 4-7 form two groups with one wave of each on every
+// SIMD; barriers cut time into half-steps and the second group runs half a step behind
+// the first, so one wave's matrix instructions overlap the other's softmax.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, wave64). Scores are computed
 // transposed, S^T = K Q^T: K rows are the A operand, queries the B operand (held in
@@ -26,10 +28,15 @@
 // step deliver exactly those 8 keys as the A operand.
 //
 // Staging. Key and value tiles move HBM -> LDS with direct loads (global_load_lds_dwordx4),
-// without passing through registers, into a 3-stage ring: the tile two ahead is in flight
-// while one is computed; physical pages are resolved one tile before that with scalar
-// loads of the page table (each wave's 8 rows of a tile lie in one page when the page size
-// is a multiple of 8).
+// without passing through registers, into a 3-stage key ring and a 4-stage value ring;
+// each group issues its loads two (first group) or three (second group) tiles ahead. The
+// plan's tile lists and, per (tile, wave), the first memory row of the wave's 8 rows are
+// staged in LDS a window of 256 tiles at a time, so the tile loop issues no memory loads
+// other than the tiles' own. When the page size is a multiple of 8 a wave's 8 rows are one
+// run in memory (one scalar base plus fixed per-lane offsets); when they are not (smaller
+// pages, a run cut by the end of the committed or live rows, an invalid page) the window
+// holds -1 and the wave resolves each row itself; absent rows load the sequence's first
+// live row in their place, and the mask gives them no weight.
 #include "bcp_internal.h"
 
 #include <type_traits>
