@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -105,7 +106,7 @@ def summarize_traffic(args):
             o = out[name]
             f.write(f"| {name.upper()}_SIZE | {o['calib_counter_bytes']:.4g} | {o['factor']:.4f} | "
                     f"{o['bytes_per_call']:.4g} | {o['attn_kernel_bytes']:.4g} |\n")
-        f.write(f"\nHBM bytes per call (fetch + write): {rec['hbm_bytes_per_call']:.4g}; kernel sources hash "
+        f.write(f"\nHBM bytes per call (fetch + write): {rec['hbm_bytes_per_call']:.4g}; kernel code hash (comments stripped) "
                 f"{rec['kernel_hash']} (bench.py reports it as roofline.traffic only while the hash matches).\n")
     print(json.dumps(rec))
 
@@ -136,9 +137,14 @@ def workload_stats(case):
 
 
 def kernel_hash():
+    """Hash of the attention kernels' code with comments and layout stripped, so that a
+    change of comments alone does not mark the committed counter summaries stale."""
     h = hashlib.sha256()
     for n in KERNEL_SOURCES + ["bcp_internal.h"]:
-        h.update(open(os.path.join(ROOT, "block_causal_paged_amd", "csrc", n), "rb").read())
+        t = open(os.path.join(ROOT, "block_causal_paged_amd", "csrc", n)).read()
+        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", "", t)
+        h.update(" ".join(t.split()).encode())
     return h.hexdigest()[:16]
 
 
