@@ -68,8 +68,12 @@ constexpr int kRowsPerWave = kTileK / kWaves;   // key rows each wave stages per
 // row are XOR-swizzled (kswz, vswz) so that the operand reads hit distinct banks.
 // The item's plan entries are staged in LDS one window of kWin tiles at a time, with, for
 // each tile and wave, the memory row of the wave's first key row when all 8 of its rows are
-// present and consecutive in memory (-1 otherwise).
+// present and consecutive in memory (-1 otherwise). Each wave owns a 4 KB output staging
+// area (32 rows x 128 bytes), through which the epilogue turns its column-held results into
+// whole 128-byte row segments before storing them.
 constexpr int kWin = 256;
+constexpr int kWinPerThread = kWin * kWaves / kThreads;   // window slots each thread stages
+constexpr int kEpRowBytes = 128;
 template <int HD>
 struct AttnSmem {
   uint16_t k[kKStages][kTileK * HD];
@@ -77,6 +81,7 @@ struct AttnSmem {
   int kblk[kVStages][kTileK];      // block id of each key of a partial tile
   int win_e[kWin];                 // the item's plan entries, one window at a time
   int win_row[kWin][kWaves];       // first memory row of each wave's 8 rows, or -1
+  float ep[kWaves][32 * kEpRowBytes / 4];   // per-wave output staging
 };
 
 // K operand reads: 16 lanes read rows r..r+15 at one logical chunk, so the swizzle spreads
@@ -371,6 +376,50 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     const int i0 = r * a.tile_q;
     const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;
 
+    // The item's tiles are processed in windows: the window's plan entries and the pages of
+    // its cached tiles are staged in LDS first, so the tile loop reads its metadata from
+    // LDS only and issues no memory loads but the tiles' own. Thread tid stages window slots
+    // tid + k * kThreads (tile slot / 8, wave slot % 8); the loads come in two rounds (plan
+    // entries, then page-table entries), issued apart from the LDS writes so that the first
+    // window's rounds overlap the query loads.
+    const bool grp_pages = a.page_size % kRowsPerWave == 0;
+    const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
+    int we[kWinPerThread], wr[kWinPerThread];
+    int tq = tid;
+    asm volatile("" : "+v"(tq));   // slot math stays here, not hoisted out of the item loop
+    auto win_load_entries = [&](int wb, int nt) {
+#pragma unroll
+      for (int k = 0; k < kWinPerThread; ++k) {
+        const int i = tq + k * kThreads;
+        we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
+      }
+    };
+    auto win_load_rows = [&](int nt) {
+#pragma unroll
+      for (int k = 0; k < kWinPerThread; ++k) {
+        const int i = tq + k * kThreads, q = i % kWaves;
+        const int vt = we[k] >> 1;
+        int row0 = -1;
+        if (i < nt * kWaves) {
+          if (vt < a.nct) {
+            const int j0 = vt * kTileK + kRowsPerWave * q;
+            if (grp_pages && j0 + kRowsPerWave <= it.kvl) {
+              int lp, slot;
+              page_split(j0, a.page_size, a.page_shift, &lp, &slot);
+              const int p = pt[lp];
+              if (p >= 0 && p < a.num_pages) row0 = p * a.page_size + slot;
+            }
+          } else {
+            const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q;
+            if (r0 + kRowsPerWave <= it.q_len) row0 = it.q0 + r0;
+          }
+        }
+        wr[k] = row0;
+      }
+    };
+    win_load_entries(ob, min(oe - ob, kWin));
+    asm volatile("" ::: "memory");   // keep the plan-entry loads ahead of the query loads
+
     // Query fragments of this lane's column (B operand of S^T = K Q^T), held in registers
     // for the whole item; padding rows read zeros.
     const int pos = i0 + rho / G, hh = rho - (rho / G) * G;
@@ -385,11 +434,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     const int qblk = !qvalid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[it.q0 + pos] : pos / a.block_size);
-    // Consume the loads here, so that no wait for them lands inside the tile loop (where it
-    // would also wait for every tile in flight).
-#pragma unroll
-    for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(qf[t]));
-    asm volatile("" ::"v"(qblk));
+    asm volatile("" ::: "memory");   // the page-table loads follow the query loads
+    win_load_rows(min(oe - ob, kWin));
 
     f32x16 o[NDB];
 #pragma unroll
@@ -397,35 +443,28 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.f;
     int n_partial = 0;
 
-    // The item's tiles are processed in windows: the window's plan entries and the pages of
-    // its cached tiles are staged in LDS first, so the tile loop reads its metadata from
-    // LDS only and issues no memory loads but the tiles' own.
-    const bool grp_pages = a.page_size % kRowsPerWave == 0;
-    const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
     for (int wb = ob; wb < oe; wb += kWin) {
       const int nt = min(oe - wb, kWin);     // tiles in this window
+      if (wb != ob) {
+        win_load_entries(wb, nt);
+        win_load_rows(nt);
+      }
       __syncthreads();   // earlier readers of LDS (previous window or item) are finished
-      for (int i = tid; i < nt * kWaves; i += kThreads) {
-        const int ti = i / kWaves, q = i - ti * kWaves;
-        const int e = list[wb + ti];
-        if (q == 0) sm.win_e[ti] = e;
-        const int vt = e >> 1;
-        int row0 = -1;
-        if (vt < a.nct) {
-          const int j0 = vt * kTileK + kRowsPerWave * q;
-          if (grp_pages && j0 + kRowsPerWave <= it.kvl) {
-            int lp, slot;
-            page_split(j0, a.page_size, a.page_shift, &lp, &slot);
-            const int p = pt[lp];
-            if (p >= 0 && p < a.num_pages) row0 = p * a.page_size + slot;
-          }
-        } else {
-          const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q;
-          if (r0 + kRowsPerWave <= it.q_len) row0 = it.q0 + r0;
+#pragma unroll
+      for (int k = 0; k < kWinPerThread; ++k) {
+        const int i = tq + k * kThreads, ti = i / kWaves, q = i % kWaves;
+        if (i < nt * kWaves) {
+          if (q == 0) sm.win_e[ti] = we[k];
+          sm.win_row[ti][q] = wr[k];
         }
-        sm.win_row[ti][q] = row0;
       }
       __syncthreads();
+      // The query loads were issued before the page-table loads just waited for, so they
+      // have landed: no wait for them falls inside the tile loop (where it would also wait
+      // for every tile in flight).
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(qf[t]));
+      asm volatile("" ::"v"(qblk));
       auto entry = [&](int t) { return t < nt ? sm.win_e[t] : -1; };
 
       // Prologue: tiles 0 .. lead-1 issued; this wave waits for all of them but the last
@@ -578,34 +617,79 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       if (!grp) __syncthreads();
     }   // window
 
-    // Epilogue. Lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4.
+    // Epilogue. Lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4 of packed
+    // row rho. Each pass writes one 128-byte column segment of the wave's 32 rows into the
+    // wave's staging area (16-byte chunk c of row r at chunk c ^ (r & 7)) and reads it back
+    // as 8 rows x 128 bytes per instruction, so every store covers whole row segments.
     const float lt = l + __shfl_xor(l, 32);
-    if (qvalid) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
-      const int64_t row = (int64_t)(it.q0 + pos) * a.Hq + (int64_t)it.g * G + hh;
-      if (pslot < 0) {
-        uint16_t* op = (uint16_t*)a.out + row * HD;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+    float* ep = sm.ep[wave];
+    // Per-lane index math is recomputed here rather than hoisted out of the item loop,
+    // where it would only hold registers.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int ec = ln & 7;                         // read-back chunk of this lane
+    const int ecol = ln & 31, ehl = ln >> 5;       // = col, hl
+    int brow[4];                                   // memory row of each read-back row, -1: none
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int k = 0; k < 4; ++k) {
+      const int rr = wave * 32 + 8 * k + (ln >> 3), pr = i0 + rr / G, hr = rr - (rr / G) * G;
+      brow[k] = pr >= it.q_len ? -1
+                : pslot < 0 ? (it.q0 + pr) * a.Hq + it.g * G + hr
+                            : pslot * kRowsPerWG + rr;
+    }
+    auto ep_slot = [&](int r, int c) { return r * (kEpRowBytes / 4) + 4 * (c ^ (r & 7)); };
+    // All passes' LDS writes and reads are issued before the first store, so the LDS round
+    // trips overlap; the wave's LDS accesses execute in order, so a pass's writes land
+    // after the previous pass's reads.
+    if (pslot < 0) {
+      uint16_t* op = (uint16_t*)a.out;
+      bf16x8 y[NDB / 2][4];
+#pragma unroll
+      for (int pb = 0; pb < NDB / 2; ++pb) {     // 64 bf16 values per row and pass
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
-            f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
-            *(bf16x4*)(op + 32 * db + 8 * v4 + 4 * hl) = __builtin_convertvector(x, bf16x4);
+            const f32x16& ob16 = o[2 * pb + j];
+            f32x4 x = {ob16[4 * v4] * inv, ob16[4 * v4 + 1] * inv, ob16[4 * v4 + 2] * inv, ob16[4 * v4 + 3] * inv};
+            *(bf16x4*)&ep[ep_slot(ecol, 4 * j + v4) + 2 * ehl] = __builtin_convertvector(x, bf16x4);
           }
-        if (hl == 0 && a.lse) a.lse[row] = lse2 * kLn2;
-      } else {
-        const int64_t slot = pslot;
-        float* pp = a.part_o + (slot * kRowsPerWG + rho) * HD;
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
-            *(f32x4*)(pp + 32 * db + 8 * v4 + 4 * hl) = x;
-          }
-        if (hl == 0) a.part_lse[slot * kRowsPerWG + rho] = lse2;
+        for (int k = 0; k < 4; ++k) y[pb][k] = *(const bf16x8*)&ep[ep_slot(8 * k + (ln >> 3), ec)];
+        asm volatile("" ::: "memory");
       }
+#pragma unroll
+      for (int pb = 0; pb < NDB / 2; ++pb)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (brow[k] >= 0) *(bf16x8*)(op + (int64_t)brow[k] * HD + 64 * pb + 8 * ec) = y[pb][k];
+      if (qvalid && ehl == 0 && a.lse) {
+        const int pe = i0 + (wave * 32 + ecol) / G, he = wave * 32 + ecol - ((wave * 32 + ecol) / G) * G;
+        a.lse[(int64_t)(it.q0 + pe) * a.Hq + (int64_t)it.g * G + he] = lse2 * kLn2;
+      }
+    } else {
+      f32x4 y[NDB][4];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {         // 32 fp32 values per row and pass
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
+          *(f32x4*)&ep[ep_slot(ecol, 2 * v4 + ehl)] = x;
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[db][k] = *(const f32x4*)&ep[ep_slot(8 * k + (ln >> 3), ec)];
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (brow[k] >= 0) *(f32x4*)(a.part_o + (int64_t)brow[k] * HD + 32 * db + 4 * ec) = y[db][k];
+      if (qvalid && ehl == 0) a.part_lse[pslot * kRowsPerWG + wave * 32 + ecol] = lse2;
     }
 
     if (a.stats && tid == 0) {
