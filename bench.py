@@ -5,8 +5,11 @@ classes, physical tile pages and the split-KV plan), attn_block_causal_paged, an
 kv_commit_block of the active blocks. Inputs are resident in HBM before timing starts.
 Before every timed step a 1 GiB buffer is overwritten so that neither L2 nor the 256 MB
 Infinity Cache still holds the KV cache (one layer's cache is cold when that layer runs
-again in a real decode step); HIP events bracket each step and each of its calls on the
-stream the kernels run on. A warm (no flush, back-to-back) figure is reported beside it.
+again in a real decode step); a pair of HIP events on the stream the kernels run on
+brackets each timed step. The per-call breakdown comes from as many further cold steps
+with events between the calls (an event between two calls idles the GPU for a few
+microseconds, so those steps are not timed as steps). A warm (no flush, back-to-back)
+figure is reported beside it.
 
 Prints one JSON line. `value` is microseconds per step (lower is better); `roofline`
 rates the dominant kernel (attention) against MI355X's HBM or bf16 matrix peak on
@@ -236,19 +239,33 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Cold steps: flush, then one step bracketed by events.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: cold steps, each a flush (outside the events) and then the whole step
+    # bracketed by one pair of events.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         flush.fill_(k & 0xFF)
-        step(evs[k])
+        evs[k][0].record()
+        step()
+        evs[k][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_us = np.array([e[0].elapsed_time(e[3]) * 1e3 for e in evs])
-    cls_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
-    attn_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
-    com_us = np.array([e[2].elapsed_time(e[3]) * 1e3 for e in evs])
+    step_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+
+    # Per-call breakdown, in as many further cold steps with events between the calls. Each
+    # event between two calls leaves the GPU idle for a few microseconds at that boundary,
+    # so these steps are not the step time; the attention call's own events give the
+    # duration the roofline uses.
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        flush.fill_(k & 0xFF)
+        step(evc[k])
+    torch.cuda.synchronize()
+    cls_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evc])
+    attn_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evc])
+    com_us = np.array([e[2].elapsed_time(e[3]) * 1e3 for e in evc])
 
     # Warm steps: back to back, no flush.
     warm_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]

@@ -217,6 +217,11 @@ int run_classify_and_plan(const bcp_meta* m, const Geo& g, uint8_t* tile_class, 
     p.num_kv_heads = m->num_kv_heads;
     p.tile_q = g.tq;
     p.tile_k = g.tk;
+    p.cu_q = m->cu_q;
+    p.kv_len = m->kv_len;
+    p.total_q = m->total_q;
+    p.max_q_len = m->max_q_len;
+    p.kv_cap = m->max_pages_per_seq * m->page_size;
     e = launch_planner(p, stream);
     if (e != hipSuccess) return hip_fail(e, "launch planner");
   }

@@ -327,8 +327,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   const int G = a.G;
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
-  const int rg = range_of_wg(blockIdx.x);
-  const int w_begin = plan[L.wg + rg], w_end = plan[L.wg + rg + 1];
+  // The range's record holds its item bounds and a copy of its first item.
+  cint32* rec = plan + L.rng + kRngWords * range_of_wg(blockIdx.x);
+  const int w_begin = rec[0], w_end = rec[1];
   const uint16_t* qg = (const uint16_t*)a.q;
   const float sl2 = a.scale_log2;
   // V transpose reads: lane (group g16 = lane/16, j = lane%16) is source lane 4*ta + tc of
@@ -366,13 +367,14 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 
   for (int item = w_begin; item < w_end; ++item) {
     Item it;
-    cint32* ip = plan + L.items + kItemWords * (int64_t)item;
+    cint32* ip = item == w_begin ? rec + 2 : plan + L.items + kItemWords * (int64_t)item;
     const int u = ip[0], ob = ip[2], oe = ip[3], pslot = ip[4];
     it.g = ip[1];
     it.s = u / a.nqt;
     const int r = u - it.s * a.nqt;
-    live_rows(a.cu_q, it.s, a.total_q, a.max_q_len, &it.q0, &it.q_len);
-    it.kvl = clampi(a.kv_len[it.s], 0, a.max_pages * a.page_size);
+    it.q0 = ip[5];       // the unit's live rows and committed length, as the planner
+    it.q_len = ip[6];    // clamped them
+    it.kvl = ip[7];
     const int i0 = r * a.tile_q;
     const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;
 

@@ -45,12 +45,17 @@ constexpr int kNoKeyBlk = INT32_MAX;    // an absent key: seen by nobody
 //   upre  [U + 1]           exclusive prefix sums of cnt (upre[U] = T)
 //   wg    [kWGs + 1]        first item of each range; wg[kWGs] = n_items
 //   items [max_items][8]    unit, kv head, first ordinal, end ordinal, partial slot (-1 when
-//                           the item is a whole pair), 0, 0, 0
+//                           the item is a whole pair), and the unit's sequence's first live
+//                           row, live-row count and committed length (clamped to the pages)
 //   split [kWGs][4]         unit, kv head, first partial slot, number of pieces
+//   rng   [kWGs][12]        per range: first item, end item, a copy of the first item's 8
+//                           words (when the range is not empty), 0, 0 -- so a workgroup
+//                           starts from one load
 constexpr int kItemWords = 8;
+constexpr int kRngWords = 12;
 
 struct PlanLayout {
-  int64_t cnt, list, upre, wg, items, split, words;
+  int64_t cnt, list, upre, wg, items, split, rng, words;
   int units, nkt, max_items;
 };
 
@@ -65,7 +70,8 @@ __host__ __device__ inline PlanLayout plan_layout(int batch, int nqt, int nkt, i
   p.wg = p.upre + p.units + 1;
   p.items = p.wg + kWGs + 1;
   p.split = p.items + kItemWords * (int64_t)p.max_items;
-  p.words = p.split + 4 * (int64_t)kWGs;
+  p.rng = p.split + 4 * (int64_t)kWGs;
+  p.words = p.rng + kRngWords * (int64_t)kWGs;
   return p;
 }
 
@@ -85,7 +91,10 @@ struct ClassifyArgs {
 
 struct PlanArgs {
   int32_t* plan;
+  const int32_t* cu_q;
+  const int32_t* kv_len;
   int batch, nqt, nkt, num_kv_heads, tile_q, tile_k;
+  int total_q, max_q_len, kv_cap;   // kv_cap = max_pages_per_seq * page_size
 };
 
 struct AttnArgs {

@@ -20,48 +20,53 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   constexpr int V4 = HD / 4;              // float4 per row
   constexpr int RPW = 256 / V4;           // rows per work item (one row per V4 threads)
   constexpr int NGRP = kRowsPerWG / RPW;  // row groups per (split unit, kv head)
-  constexpr int MAXC = 8;                 // splits merged per pass, loads issued together
+  constexpr int MAXC = 8;                 // splits whose loads are issued together
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
-  const int n_work = plan[1] * NGRP;
   const int tid = threadIdx.x, d4 = tid % V4, rr = tid / V4;
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+  // The loads of a work item form two rounds: its split record (with the work count), then
+  // the sequence's live rows and every partial result at once; the partial addresses do not
+  // depend on the live rows, and rows past the sequence's live rows are not stored.
+  for (int w = blockIdx.x; w < kWGs * NGRP; w += gridDim.x) {
     const int grp = w % NGRP, e = w / NGRP;
-    cint32* sp = plan + L.split + 4 * (int64_t)e;
+    cint32* sp = plan + L.split + 4 * (int64_t)e;   // inside the kWGs split records
     const int u = sp[0], g = sp[1], ps0 = sp[2], n = sp[3];
+    if (w >= plan[1] * NGRP) break;
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
+    const int rho = grp * RPW + rr;
+    float lc[MAXC];
+    f32x4 oc[MAXC];
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int64_t slot = ps0 + min(k, n - 1);
+      lc[k] = a.part_lse[slot * kRowsPerWG + rho];
+      oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+    }
     int q0, q_len;
     live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
-    const int rho = grp * RPW + rr;
     const int pos = r * a.tile_q + rho / a.G, hh = rho - (rho / a.G) * a.G;
-    if (pos >= q_len) continue;
-    // Pass 1: the largest partial LSE. Pass 2: the weighted sum, MAXC splits at a time with
-    // all their loads in flight together.
     float M = -INFINITY;
-    for (int c = 0; c < n; ++c)
-      M = fmaxf(M, a.part_lse[(int64_t)(ps0 + c) * kRowsPerWG + rho]);
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) M = fmaxf(M, lc[k]);   // repeats of the last split change nothing
+    for (int c = MAXC; c < n; ++c) M = fmaxf(M, a.part_lse[(int64_t)(ps0 + c) * kRowsPerWG + rho]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (M != -INFINITY) {
-      for (int c0 = 0; c0 < n; c0 += MAXC) {
-        float lc[MAXC];
-        f32x4 oc[MAXC];
 #pragma unroll
-        for (int k = 0; k < MAXC; ++k) {
-          const int c = min(c0 + k, n - 1);
-          const int64_t slot = ps0 + c;
-          lc[k] = a.part_lse[slot * kRowsPerWG + rho];
-          oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
-        }
-#pragma unroll
-        for (int k = 0; k < MAXC; ++k) {
-          const float wc = c0 + k < n ? __builtin_amdgcn_exp2f(lc[k] - M) : 0.f;
-          acc += wc * oc[k];
-          wsum += wc;
-        }
+      for (int k = 0; k < MAXC; ++k) {
+        const float wc = k < n ? __builtin_amdgcn_exp2f(lc[k] - M) : 0.f;
+        acc += wc * oc[k];
+        wsum += wc;
+      }
+      for (int c = MAXC; c < n; ++c) {
+        const int64_t slot = ps0 + c;
+        const float wc = __builtin_amdgcn_exp2f(a.part_lse[slot * kRowsPerWG + rho] - M);
+        acc += wc * *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+        wsum += wc;
       }
       acc *= 1.f / wsum;
     }
+    if (pos >= q_len) continue;
     const int64_t row = (int64_t)(q0 + pos) * a.Hq + (int64_t)g * a.G + hh;
     if constexpr (BF16_OUT) {
       *(bf16x4*)((uint16_t*)a.out + row * HD + 4 * d4) = __builtin_convertvector(acc, bf16x4);

@@ -259,6 +259,26 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
     for (int u = tid; u < units; u += kPlanThreads) s_cnt[u] = plan[L.cnt + u];
   __syncthreads();
   auto cnt_of = [&](int u) { return in_lds ? s_cnt[u] : plan[L.cnt + u]; };
+  // Writes item `idx` (unit u, kv head g, ordinals [ob, oe), partial slot ps) with the
+  // unit's live rows and committed length, which the attention kernel then reads with the
+  // item instead of loading them; the item that opens range r is also copied into the
+  // range's record.
+  auto put_item = [&](int64_t idx, int u, int g, int ob, int oe, int ps, int opens) {
+    const int sq = u / a.nqt;
+    int q0, ql;
+    live_rows(a.cu_q, sq, a.total_q, a.max_q_len, &q0, &ql);
+    const int w[kItemWords] = {u, g, ob, oe, ps, q0, ql, clampi(a.kv_len[sq], 0, a.kv_cap)};
+    int* it = plan + L.items + kItemWords * idx;
+#pragma unroll
+    for (int i = 0; i < kItemWords; ++i) it[i] = w[i];
+    if (opens >= 0) {
+      int* rec = plan + L.rng + kRngWords * (int64_t)opens;
+#pragma unroll
+      for (int i = 0; i < kItemWords; ++i) rec[2 + i] = w[i];
+      rec[10] = 0;
+      rec[11] = 0;
+    }
+  };
 
   // Prefix sums of the per-unit tile counts.
   const int upt = (units + kPlanThreads - 1) / kPlanThreads;
@@ -310,15 +330,8 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
     const bool split = n > 1;
     const Int3 at = block_scan3_excl(Int3{n, split ? n : 0, split ? 1 : 0}, scan_lds, &all);
     for (int k = 0; k < n; ++k) {
-      int* it = plan + L.items + kItemWords * (int64_t)(at.x + k);
-      it[0] = u;
-      it[1] = g;
-      it[2] = (int)(((long long)k * cnt) / n);
-      it[3] = (int)(((long long)(k + 1) * cnt) / n);
-      it[4] = split ? at.y + k : -1;
-      it[5] = 0;
-      it[6] = 0;
-      it[7] = 0;
+      put_item(at.x + k, u, g, (int)(((long long)k * cnt) / n), (int)(((long long)(k + 1) * cnt) / n),
+               split ? at.y + k : -1, at.x + k);
       wg_first[at.x + k] = at.x + k;
     }
     if (split) {
@@ -367,16 +380,9 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
       for (int k = 0; k < n; ++k) {
         const unsigned r = rf + k;
         const unsigned lo = max(b(r), S), hi = min(b(r + 1), S + cnt);
-        int* it = plan + L.items + kItemWords * (int64_t)(at.x + k);
-        it[0] = u;
-        it[1] = g;
-        it[2] = (int)(lo - S);
-        it[3] = (int)(hi - S);
-        it[4] = split ? at.y + k : -1;
-        it[5] = 0;
-        it[6] = 0;
-        it[7] = 0;
-        if (lo == b(r)) wg_first[r] = at.x + k;   // the piece that opens range r
+        const bool opens = lo == b(r);   // the piece that opens range r
+        put_item(at.x + k, u, g, (int)(lo - S), (int)(hi - S), split ? at.y + k : -1, opens ? (int)r : -1);
+        if (opens) wg_first[r] = at.x + k;
       }
       if (split) {
         int* sp = plan + L.split + 4 * (int64_t)at.z;
@@ -419,10 +425,19 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
     int later = __shfl_down(x, 1);
     if (lane == 63) later = INT32_MAX;
     for (int w = wave + 1; w < kPlanThreads / 64; ++w) later = min(later, wave_min[w]);
+    __syncthreads();   // every thread has read wg_first
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int w = tid * PER + k;
-      if (w <= kWGs) plan[L.wg + w] = min(v[k], later);
+      if (w <= kWGs) {
+        plan[L.wg + w] = min(v[k], later);
+        wg_first[w] = min(v[k], later);
+      }
+    }
+    __syncthreads();
+    for (int w = tid; w < kWGs; w += kPlanThreads) {
+      plan[L.rng + kRngWords * (int64_t)w] = wg_first[w];
+      plan[L.rng + kRngWords * (int64_t)w + 1] = wg_first[w + 1];
     }
   }
   if (tid == 0) {

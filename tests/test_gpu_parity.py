@@ -350,6 +350,19 @@ def test_plan_ranges_cover_every_visit_once(workloads, n):
             assert all(a[1] == b[0] for a, b in zip(pieces, pieces[1:]))
             assert (len(pieces) == 1) == (pieces[0][2] < 0)
     assert len(slots) == len(set(slots)) and (not slots or max(slots) < MAX_SLOTS)
+    # Each item carries its sequence's live rows and committed length (clamped to the pages).
+    for it in items:
+        s = int(it[0]) // nqt
+        kv_cap = case.max_pages_per_seq * case.page_size
+        assert list(it[5:8]) == [case.cu_q[s], case.cu_q[s + 1] - case.cu_q[s], min(case.kv_len[s], kv_cap)]
+    # Range records: item bounds, and a copy of the first item of every non-empty range.
+    rng_off = split_off + 4 * N_WGS
+    rec = w[rng_off:rng_off + 12 * N_WGS].reshape(N_WGS, 12)
+    np.testing.assert_array_equal(rec[:, 0], wg[:-1])
+    np.testing.assert_array_equal(rec[:, 1], wg[1:])
+    for k in range(N_WGS):
+        if wg[k] < wg[k + 1]:
+            np.testing.assert_array_equal(rec[k, 2:10], items[wg[k]])
     splits = w[split_off:split_off + 4 * n_split].reshape(n_split, 4)
     for u, g, ps0, npieces in splits:
         assert [p[2] for p in covered[(int(u), int(g))]] == list(range(ps0, ps0 + npieces))
