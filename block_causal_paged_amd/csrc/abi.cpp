@@ -206,22 +206,22 @@ int run_classify_and_plan(const bcp_meta* m, const Geo& g, uint8_t* tile_class, 
   a.phys_page = phys_page;
   a.plan = plan;
   a.grid_q = std::max(g.nqt, 1);
+  PlanArgs p{};
+  p.plan = plan;
+  p.batch = m->batch;
+  p.nqt = g.nqt;
+  p.nkt = g.nkt;
+  p.num_kv_heads = m->num_kv_heads;
+  p.tile_q = g.tq;
+  p.tile_k = g.tk;
+  p.cu_q = m->cu_q;
+  p.kv_len = m->kv_len;
+  p.total_q = m->total_q;
+  p.max_q_len = m->max_q_len;
+  p.kv_cap = m->max_pages_per_seq * m->page_size;
   hipError_t e = launch_classify(a, stream);
   if (e != hipSuccess) return hip_fail(e, "launch classify");
   if (plan) {
-    PlanArgs p{};
-    p.plan = plan;
-    p.batch = m->batch;
-    p.nqt = g.nqt;
-    p.nkt = g.nkt;
-    p.num_kv_heads = m->num_kv_heads;
-    p.tile_q = g.tq;
-    p.tile_k = g.tk;
-    p.cu_q = m->cu_q;
-    p.kv_len = m->kv_len;
-    p.total_q = m->total_q;
-    p.max_q_len = m->max_q_len;
-    p.kv_cap = m->max_pages_per_seq * m->page_size;
     e = launch_planner(p, stream);
     if (e != hipSuccess) return hip_fail(e, "launch planner");
   }

@@ -63,10 +63,10 @@ __device__ int block_max(int v, int* lds) {
 
 constexpr int kClsLdsTiles = 2048;   // key tiles whose mode-B block-id ranges fit in LDS
 
-__global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
+// Classifies q-tile r of sequence s (one workgroup of 256 threads; every thread calls it).
+__device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
   __shared__ int red[2][4];
   __shared__ int scan_lds[16];
-  const int s = blockIdx.x / a.grid_q, r = blockIdx.x - (blockIdx.x / a.grid_q) * a.grid_q;
   const bool has_tiles = r < a.nqt;     // false only for the phys_page-only launch of an empty grid
   const int u = s * a.nqt + r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -204,9 +204,14 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
+  classify_unit(a, blockIdx.x / a.grid_q, blockIdx.x % a.grid_q);
+}
+
 // Exclusive prefix sums of three values at once over a workgroup of kPlanThreads.
 constexpr int kPlanThreads = 256;
 constexpr int kPlanLdsUnits = 4096;
+constexpr int kPlanLdsSeqs = 1024;   // sequences whose live rows and length are staged in LDS
 struct Int3 {
   int x, y, z;
 };
@@ -245,7 +250,7 @@ __device__ Int3 block_scan3_excl(Int3 v, Int3* lds, Int3* total) {
 // One workgroup turns the per-unit tile counts into the ranges of the step's visits and
 // the items (whole or partial (unit, kv head) pairs) that make them up. Each thread takes
 // a contiguous run of units, then of pairs, so one scan orders everything.
-__global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
+__device__ void plan_step(const PlanArgs& a) {
   __shared__ Int3 scan_lds[kPlanThreads / 64];
   __shared__ int wg_first[kWGs + 1];
   __shared__ int s_cnt[kPlanLdsUnits], s_upre[kPlanLdsUnits];
@@ -254,9 +259,17 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
   const int units = L.units, hkv = a.num_kv_heads;
   const int tid = threadIdx.x;
   // Per-unit counts and their prefix sums live in LDS when they fit (else in the plan).
+  // So are each sequence's live rows and committed length, which every item carries.
+  __shared__ int s_seq[kPlanLdsSeqs][3];
   const bool in_lds = units <= kPlanLdsUnits;
+  const bool seq_lds = a.batch <= kPlanLdsSeqs;
   if (in_lds)
     for (int u = tid; u < units; u += kPlanThreads) s_cnt[u] = plan[L.cnt + u];
+  if (seq_lds)
+    for (int sq = tid; sq < a.batch; sq += kPlanThreads) {
+      live_rows(a.cu_q, sq, a.total_q, a.max_q_len, &s_seq[sq][0], &s_seq[sq][1]);
+      s_seq[sq][2] = clampi(a.kv_len[sq], 0, a.kv_cap);
+    }
   __syncthreads();
   auto cnt_of = [&](int u) { return in_lds ? s_cnt[u] : plan[L.cnt + u]; };
   // Writes item `idx` (unit u, kv head g, ordinals [ob, oe), partial slot ps) with the
@@ -265,9 +278,16 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
   // range's record.
   auto put_item = [&](int64_t idx, int u, int g, int ob, int oe, int ps, int opens) {
     const int sq = u / a.nqt;
-    int q0, ql;
-    live_rows(a.cu_q, sq, a.total_q, a.max_q_len, &q0, &ql);
-    const int w[kItemWords] = {u, g, ob, oe, ps, q0, ql, clampi(a.kv_len[sq], 0, a.kv_cap)};
+    int q0, ql, kvl;
+    if (seq_lds) {
+      q0 = s_seq[sq][0];
+      ql = s_seq[sq][1];
+      kvl = s_seq[sq][2];
+    } else {
+      live_rows(a.cu_q, sq, a.total_q, a.max_q_len, &q0, &ql);
+      kvl = clampi(a.kv_len[sq], 0, a.kv_cap);
+    }
+    const int w[kItemWords] = {u, g, ob, oe, ps, q0, ql, kvl};
     int* it = plan + L.items + kItemWords * idx;
 #pragma unroll
     for (int i = 0; i < kItemWords; ++i) it[i] = w[i];
@@ -310,19 +330,43 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
     const int pr = tid;
     const int u = pr < pairs ? pr % units : 0, g = pr < pairs ? pr / units : 0;
     const int cnt = pr < pairs ? cnt_of(u) : 0;
-    Int3 t3;
-    auto chunks = [&](int c) {
-      block_scan3_excl(Int3{(cnt + c - 1) / c, 0, 0}, scan_lds, &t3);
-      return t3.x;
-    };
+    // The search tests kCand chunk lengths per round: the chunk counts of all candidates
+    // are summed over the pairs at once (one reduction), and the interval shrinks to the
+    // gap between the last candidate that gives too many chunks and the next one.
+    constexpr int kCand = 8;
+    __shared__ int cand_lds[kPlanThreads / 64][kCand];
     const int cmax = block_max(cnt, (int*)scan_lds);
     int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
-    if (cmax > c && chunks(c) > kWGs) {
-      int lo = c, hi = cmax;   // too many chunks at lo; one per pair (<= kWGs) at hi
+    if (cmax > c) {
+      int lo = c - 1, hi = cmax;   // too many chunks at lo (or lo below the start); <= kWGs at hi
       while (hi - lo > 1) {
-        const int mid = lo + (hi - lo) / 2;
-        if (chunks(mid) <= kWGs) hi = mid;
-        else lo = mid;
+        const int step = (hi - lo + kCand) / (kCand + 1);   // candidates lo + step*(j+1) < hi
+        int n[kCand];
+#pragma unroll
+        for (int j = 0; j < kCand; ++j) {
+          const int cj = min(lo + step * (j + 1), hi);
+          n[j] = (cnt + cj - 1) / cj;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) n[j] += __shfl_xor(n[j], o);
+        }
+        const int lane = tid & 63, wave = tid >> 6;
+        if (lane == 0)
+#pragma unroll
+          for (int j = 0; j < kCand; ++j) cand_lds[wave][j] = n[j];
+        __syncthreads();
+        int new_lo = lo, new_hi = hi;
+#pragma unroll
+        for (int j = kCand - 1; j >= 0; --j) {
+          int tot = 0;
+#pragma unroll
+          for (int w = 0; w < kPlanThreads / 64; ++w) tot += cand_lds[w][j];
+          const int cj = min(lo + step * (j + 1), hi);
+          if (tot <= kWGs) new_hi = cj;        // the smallest fitting candidate wins
+          else if (new_lo == lo) new_lo = cj;  // the largest failing candidate
+        }
+        __syncthreads();
+        lo = new_lo;   // chunk counts fall as the length grows, so new_lo < new_hi
+        hi = new_hi;
       }
       c = hi;
     }
@@ -451,6 +495,8 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) {
     plan[7] = a.nkt;
   }
 }
+
+__global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) { plan_step(a); }
 
 }  // namespace
 

@@ -257,7 +257,8 @@ def test_tile_classes_page_figures(name, spec, tq, tk):
     check_tiles(case, tq, tk)
 
 
-def check_tiles(case, tq, tk):
+def check_tiles(case, tq, tk, with_plan=False):
+    # With a plan requested too, the classes and pages must be the same.
     dc = DeviceCase(case)
     meta = bcp.StepMeta(**dc.meta_kwargs(), tile_q=tq, tile_k=tk, check=True)
     nqt, nkt = bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
@@ -265,7 +266,8 @@ def check_tiles(case, tq, tk):
     ppt = max(1, tk // case.page_size)
     tc = torch.full((case.batch, nqt, nkt), 255, dtype=torch.uint8, device="cuda")
     pp = torch.full((case.batch, nct, ppt), -7, dtype=torch.int32, device="cuda") if nct else None
-    bcp.build_tile_mask(meta, tile_class=tc, phys_page=pp)
+    plan_t = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda") if with_plan else None
+    bcp.build_tile_mask(meta, tile_class=tc, phys_page=pp, plan=plan_t)
     torch.cuda.synchronize()
     ref = oracle_tiles(case, tq, tk)
     got = tc.cpu().numpy()
@@ -283,11 +285,15 @@ def check_tiles(case, tq, tk):
 def test_tile_classes_random(seed, mode, tq, tk, P):
     case = small_case(seed, G=4, d=64, D=5, P=P, mode=mode, max_q=150, max_kv=400)
     check_tiles(case, tq, tk)
+    if (tq, tk) == (64, 64):
+        check_tiles(case, tq, tk, with_plan=True)
 
 
-@pytest.mark.parametrize("n", [2, 4, 5, 3])
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 3])
 def test_tile_classes_workloads(workloads, n):
     case = workloads(n)
+    G = case.num_q_heads // case.num_kv_heads
+    check_tiles(case, 256 // G, 64, with_plan=True)
     got = check_tiles(case, 64, 64)
     if n == 3:
         assert (got == bcp.BCP_TILE_FULL).sum() == 4 * 8256 and (got == bcp.BCP_TILE_PARTIAL).sum() == 0
@@ -308,7 +314,7 @@ def _plan_words(case, dc):
     return plan_t.view(torch.int32).cpu().numpy(), bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
 
 
-@pytest.mark.parametrize("n", [2, 4, 5, 3])
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 3])
 def test_plan_ranges_cover_every_visit_once(workloads, n):
     case = workloads(n)
     w, nqt, nkt = _plan_words(case, DeviceCase(case))
