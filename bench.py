@@ -164,32 +164,34 @@ def traffic_from_profile(cfg):
 
 
 def cpu_baseline(case, budget_s):
-    """The oracle as it stands, on whole sequences of the same workload until the budget is
-    spent; scaled to microseconds per full step by the fraction of query rows covered."""
+    """The oracle as it stands, over whole sequences of the same workload in order, pass
+    after pass, until the budget is spent; scaled to microseconds per full step by the
+    number of query rows covered."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    order = list(range(case.batch))
     t0 = time.perf_counter()
     rows_done = 0
-    seqs = []
-    for s in order:
+    seqs = 0
+    while True:
+        s = seqs % case.batch
         oracle.attention_rows(case.q, case.k_new, case.v_new, case.k_cache, case.v_cache, case.cu_q,
                               case.kv_len, case.page_table, case.page_size, case.num_pages, s,
                               block_size=case.block_size, q_blk=case.q_blk, kv_blk=case.kv_blk)
         rows_done += int(case.q_lens[s])
-        seqs.append(s)
+        seqs += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    frac = rows_done / max(1, case.total_q)
-    per_step_us = dt / frac * 1e6
+    steps = rows_done / max(1, case.total_q)
+    per_step_us = dt / steps * 1e6
+    what = (f"{seqs // case.batch} full passes over the {case.batch} sequences" + (f" and {seqs % case.batch} more"
+            if seqs % case.batch else "")) if seqs >= case.batch else f"sequences 0..{seqs - 1} of {case.batch}"
     return {"value": per_step_us, "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"float64 NumPy oracle on sequences {seqs[0]}..{seqs[-1]} ({len(seqs)} of "
-                      f"{case.batch}, {frac:.1%} of query rows, all heads) in {dt:.1f} s, scaled to the "
-                      f"full step"}
+            "sample": f"float64 NumPy oracle, all heads, on {what} ({steps:.3g} steps of query rows) "
+                      f"in {dt:.1f} s, scaled to one step"}
 
 
 def main():
