@@ -527,11 +527,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
             for (int kb = 0; kb < 2; ++kb)      // alternate the two accumulators
               sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][kb], qf[s], s == 0 ? f32x16{} : sc[kb], 0, 0, 0);
         }
-        // Interleave: a few operand reads first, then one matrix instruction per read
+        // Interleave: ten operand reads first, then one matrix instruction per read
         // (K: one b128 read per instruction; V: two transpose reads per instruction).
         constexpr int NR = (WITH_S ? 2 * NT : 0) + (WITH_PV ? 8 * NDB : 0);
         constexpr int NM = (WITH_S ? 2 * NT : 0) + (WITH_PV ? 4 * NDB : 0);
-        constexpr int AHEAD = 4;
+        constexpr int AHEAD = NR < 10 ? NR : 10;
         __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
         interleave<NM, NR, AHEAD>();
       };

@@ -212,6 +212,9 @@ __global__ __launch_bounds__(256) void classify_kernel(ClassifyArgs a) {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanLdsUnits = 4096;
 constexpr int kPlanLdsSeqs = 1024;   // sequences whose live rows and length are staged in LDS
+// Start-up cost of a work item (its first loads and its epilogue) in key-tile visits, as
+// the stream-K cut counts it: about 10 us against about 2 us per visit.
+constexpr unsigned kItemCost = 5;
 struct Int3 {
   int x, y, z;
 };
@@ -253,7 +256,7 @@ __device__ Int3 block_scan3_excl(Int3 v, Int3* lds, Int3* total) {
 __device__ void plan_step(const PlanArgs& a) {
   __shared__ Int3 scan_lds[kPlanThreads / 64];
   __shared__ int wg_first[kWGs + 1];
-  __shared__ int s_cnt[kPlanLdsUnits], s_upre[kPlanLdsUnits];
+  __shared__ int s_cnt[kPlanLdsUnits], s_upre[kPlanLdsUnits], s_nepre[kPlanLdsUnits];
   int* plan = a.plan;
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.num_kv_heads);
   const int units = L.units, hkv = a.num_kv_heads;
@@ -303,14 +306,23 @@ __device__ void plan_step(const PlanArgs& a) {
   // Prefix sums of the per-unit tile counts.
   const int upt = (units + kPlanThreads - 1) / kPlanThreads;
   const int u0 = min(units, tid * upt), u1 = min(units, u0 + upt);
-  int mine = 0;
-  for (int u = u0; u < u1; ++u) mine += cnt_of(u);
+  // (With them, the number of units with tiles before each unit.)
+  int mine = 0, mine_ne = 0;
+  for (int u = u0; u < u1; ++u) {
+    mine += cnt_of(u);
+    mine_ne += cnt_of(u) > 0;
+  }
   Int3 tot;
-  int run = block_scan3_excl(Int3{mine, 0, 0}, scan_lds, &tot).x;
+  const Int3 run3 = block_scan3_excl(Int3{mine, mine_ne, 0}, scan_lds, &tot);
+  int run = run3.x, run_ne = run3.y;
   for (int u = u0; u < u1; ++u) {
     plan[L.upre + u] = run;
-    if (in_lds) s_upre[u] = run;
+    if (in_lds) {
+      s_upre[u] = run;
+      s_nepre[u] = run_ne;
+    }
     run += cnt_of(u);
+    run_ne += cnt_of(u) > 0;
   }
   const int total_tiles = tot.x;
   if (tid == 0) plan[L.upre + units] = total_tiles;
@@ -387,19 +399,27 @@ __device__ void plan_step(const PlanArgs& a) {
     }
     n_wg = max(1, all.x);
   } else {
-    // Range r covers visits [b(r), b(r+1)) of W = T * Hkv, for n_wg <= kWGs ranges: the
-    // first `rem` ranges have q + 1 visits, the others q. (32-bit: the plan supports steps of
-    // fewer than 2^31 visits.)
-    n_wg = max(1u, min((unsigned)kWGs, W / kMinChunk));
-    const unsigned q = W / n_wg, rem = W - q * n_wg, big = rem * (q + 1);
+    // The pairs, head-major, are laid end to end in a virtual sequence in which each pair
+    // with tiles is its kItemCost start-up positions (standing for the work item's fixed
+    // cost: its first loads and its epilogue) followed by its visits. Range r covers
+    // positions [b(r), b(r+1)) of the Wv positions, for n_wg <= kWGs ranges: the first `rem`
+    // ranges have q + 1 positions, the others q. So a range that starts more items gets
+    // fewer visits. (32-bit: the plan supports steps of fewer than 2^31 positions.)
+    const unsigned C = in_lds ? kItemCost : 0, NE = (unsigned)tot.y;
+    const unsigned Wv = W + C * (unsigned)hkv * NE;
+    n_wg = max(1u, min((unsigned)kWGs, Wv / kMinChunk));
+    const unsigned q = Wv / n_wg, rem = Wv - q * n_wg, big = rem * (q + 1);
     auto b = [&](unsigned r) { return r * q + min(r, rem); };
     auto range_of = [&](unsigned x) { return x < big ? x / (q + 1) : rem + (x - big) / q; };
-    // Pair pr = (kv head g, unit u), head-major: its visits start at S = g*T + upre[u].
-    auto pair_info = [&](int pr, int* u, int* g, int* cnt, unsigned* S, unsigned* rf) {
+    // Pair pr = (kv head g, unit u): its start-up positions begin at
+    // Sv = g*(T + C*NE) + upre[u] + C*nepre[u], its visits at S = Sv + C.
+    auto pair_info = [&](int pr, int* u, int* g, int* cnt, unsigned* S, unsigned* rf, unsigned* Sv) {
       *g = pr / units;
       *u = pr - *g * units;
       *cnt = cnt_of(*u);
-      *S = (unsigned)*g * (unsigned)total_tiles + (unsigned)upre_of(*u);
+      *Sv = (unsigned)*g * ((unsigned)total_tiles + C * NE) + (unsigned)upre_of(*u) +
+            (C ? C * (unsigned)s_nepre[*u] : 0u);
+      *S = *Sv + C;
       *rf = *cnt > 0 ? range_of(*S) : 0;
       return *cnt > 0 ? (int)(range_of(*S + *cnt - 1) - *rf) + 1 : 0;   // pieces
     };
@@ -409,8 +429,8 @@ __device__ void plan_step(const PlanArgs& a) {
     Int3 own = {0, 0, 0};   // items, partial slots, split pairs of this thread's pairs
     for (int pr = p0; pr < p1; ++pr) {
       int u, g, cnt;
-      unsigned S, rf;
-      const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+      unsigned S, rf, Sv;
+      const int n = pair_info(pr, &u, &g, &cnt, &S, &rf, &Sv);
       own.x += n;
       own.y += n > 1 ? n : 0;
       own.z += n > 1 ? 1 : 0;
@@ -418,13 +438,16 @@ __device__ void plan_step(const PlanArgs& a) {
     Int3 at = block_scan3_excl(own, scan_lds, &all);
     for (int pr = p0; pr < p1; ++pr) {
       int u, g, cnt;
-      unsigned S, rf;
-      const int n = pair_info(pr, &u, &g, &cnt, &S, &rf);
+      unsigned S, rf, Sv;
+      const int n = pair_info(pr, &u, &g, &cnt, &S, &rf, &Sv);
       const bool split = n > 1;
       for (int k = 0; k < n; ++k) {
         const unsigned r = rf + k;
         const unsigned lo = max(b(r), S), hi = min(b(r + 1), S + cnt);
-        const bool opens = lo == b(r);   // the piece that opens range r
+        // The piece opens range r (is its first item) when no earlier pair's visits lie in
+        // it: later pieces start at b(r); the first one when the pair's start-up positions
+        // begin at or before b(r) (the previous pair's positions end where they begin).
+        const bool opens = k > 0 || Sv <= b(r);
         put_item(at.x + k, u, g, (int)(lo - S), (int)(hi - S), split ? at.y + k : -1, opens ? (int)r : -1);
         if (opens) wg_first[r] = at.x + k;
       }

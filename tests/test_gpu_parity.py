@@ -303,7 +303,7 @@ def test_tile_classes_workloads(workloads, n):
 # its internal header, mirrored here): the (kv head, unit, key tile) visits are cut into
 # contiguous ranges of near-equal length, one per workgroup; every pair's tiles are covered
 # exactly once, in order; pieces of a cut pair own distinct partial slots.
-N_WGS, ITEM_WORDS, MAX_SLOTS = 256, 8, 512
+N_WGS, ITEM_WORDS, MAX_SLOTS, ITEM_COST = 256, 8, 512, 5
 
 
 def _plan_words(case, dc):
@@ -375,8 +375,14 @@ def test_plan_ranges_cover_every_visit_once(workloads, n):
     used = loads[:n_wg]
     assert loads[n_wg:].sum() == 0 and used.sum() == total * hkv
     if U * hkv > N_WGS:
-        # Many pairs: the visits are cut into ranges that differ by at most one visit.
-        assert used.max() - used.min() <= 1
+        # Many pairs: the visits, each pair preceded by ITEM_COST start-up positions, are cut
+        # into ranges that differ by at most one position. Counting ITEM_COST for each pair
+        # that starts in a range is off by at most ITEM_COST at either end.
+        starts = np.zeros(N_WGS, dtype=np.int64)
+        for k in range(N_WGS):
+            starts[k] = sum(1 for it in items[wg[k]:wg[k + 1]] if it[2] == 0)
+        cost = (loads + ITEM_COST * starts)[:n_wg]
+        assert cost.max() - cost.min() <= 2 * ITEM_COST + 1
     else:
         # Few pairs: each is cut into near-equal chunks, one per range.
         assert n_wg == n_items and used.max() <= 1.5 * used.mean() + 1
