@@ -26,16 +26,35 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then each row's total is added to
+// the rows after it (row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_scan_incl(x), 63); }
+// Maximum over the wave's lanes of non-negative values (0 fills the shifted-in lanes).
+__device__ __forceinline__ int wave_max_nonneg(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // Exclusive prefix sum over the workgroup (blockDim.x a multiple of 64, at most 1024).
 // Returns this thread's exclusive prefix; *total receives the workgroup sum.
 __device__ int block_scan_excl(int v, int* lds16, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_scan_incl(v);
   if (lane == 63) lds16[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
@@ -49,10 +68,11 @@ __device__ int block_scan_excl(int v, int* lds16, int* total) {
   return before + x - v;
 }
 
-// Maximum over the workgroup (every thread gets it); lds holds one int per wave.
-__device__ int block_max(int v, int* lds) {
+// Maximum over the workgroup of non-negative values (every thread gets it); lds holds one
+// int per wave.
+__device__ int block_max_nonneg(int v, int* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = wave_max(v);
+  v = wave_max_nonneg(v);
   if (lane == 0) lds[wave] = v;
   __syncthreads();
   int m = lds[0];
@@ -220,16 +240,7 @@ struct Int3 {
 };
 __device__ Int3 block_scan3_excl(Int3 v, Int3* lds, Int3* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Int3 s = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(s.x, o), b = __shfl_up(s.y, o), c = __shfl_up(s.z, o);
-    if (lane >= o) {
-      s.x += a;
-      s.y += b;
-      s.z += c;
-    }
-  }
+  const Int3 s = {wave_scan_incl(v.x), wave_scan_incl(v.y), wave_scan_incl(v.z)};
   if (lane == 63) lds[wave] = s;
   __syncthreads();
   Int3 before = {0, 0, 0}, all = {0, 0, 0};
@@ -343,28 +354,27 @@ __device__ void plan_step(const PlanArgs& a) {
     const int u = pr < pairs ? pr % units : 0, g = pr < pairs ? pr / units : 0;
     const int cnt = pr < pairs ? cnt_of(u) : 0;
     // The search tests kCand chunk lengths per round: the chunk counts of all candidates
-    // are summed over the pairs at once (one reduction), and the interval shrinks to the
-    // gap between the last candidate that gives too many chunks and the next one.
+    // are summed over the pairs at once (wave sums, then one exchange through LDS). The
+    // first round tries the kCand lengths from the lower bound up, which settles the usual
+    // case; later rounds spread the candidates over the remaining interval, which shrinks
+    // to the gap between the last length that gives too many chunks and the next one.
     constexpr int kCand = 8;
     __shared__ int cand_lds[kPlanThreads / 64][kCand];
-    const int cmax = block_max(cnt, (int*)scan_lds);
+    const int cmax = block_max_nonneg(cnt, (int*)scan_lds);
     int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
     if (cmax > c) {
       int lo = c - 1, hi = cmax;   // too many chunks at lo (or lo below the start); <= kWGs at hi
+      bool first = true;
       while (hi - lo > 1) {
-        const int step = (hi - lo + kCand) / (kCand + 1);   // candidates lo + step*(j+1) < hi
-        int n[kCand];
+        const int step = first ? 1 : (hi - lo + kCand) / (kCand + 1);   // lo + step*(j+1)
+        first = false;
+        const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
         for (int j = 0; j < kCand; ++j) {
           const int cj = min(lo + step * (j + 1), hi);
-          n[j] = (cnt + cj - 1) / cj;
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) n[j] += __shfl_xor(n[j], o);
+          const int nj = wave_sum((cnt + cj - 1) / cj);
+          if (lane == 0) cand_lds[wave][j] = nj;
         }
-        const int lane = tid & 63, wave = tid >> 6;
-        if (lane == 0)
-#pragma unroll
-          for (int j = 0; j < kCand; ++j) cand_lds[wave][j] = n[j];
         __syncthreads();
         int new_lo = lo, new_hi = hi;
 #pragma unroll
