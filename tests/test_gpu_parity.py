@@ -240,6 +240,38 @@ def test_C3_prefill_sampled(workloads):
     assert torch.isfinite(out.float()).all()
 
 
+def test_items_longer_than_one_window():
+    # 4 sequences x 65 q-tiles, each over 16384 committed keys and a 4160-row prompt, one kv
+    # head: more than 256 (unit, head) pairs and more than 65536 visits, so the stream-K
+    # ranges hold over 256 tiles and some items span two metadata windows of the kernel.
+    rng = np.random.default_rng(4242)
+    case = make_case(4242, dtype="bf16", num_q_heads=4, num_kv_heads=1, head_dim=64, block_size=64,
+                     page_size=64, q_lens=[4160] * 4, kv_lens=[16384] * 4, qkv_std=1 / 8, rng=rng)
+    dc = DeviceCase(case)
+    w, nqt, nkt = _plan_words(case, dc)
+    U = case.batch * nqt
+    items_off = 8 + U + U * nkt + U + 1 + N_WGS + 1
+    items = w[items_off:items_off + ITEM_WORDS * int(w[0])].reshape(-1, ITEM_WORDS)
+    assert (items[:, 3] - items[:, 2]).max() > 256
+    rows = {s: np.unique(np.concatenate([[0, 63, 64, 4159], rng.integers(0, 4160, 12)])) for s in range(4)}
+    O_ref, L_ref = oracle_attention(case, rows=rows)
+    out, lse = run_attn(dc)
+    assert_close(out, O_ref, "bf16", lse, L_ref, what="two-window items")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sequences_without_live_rows(dtype):
+    # Sequences with no live rows (and one with neither live rows nor cache) among others:
+    # they own no q-tile work and must not disturb the rest.
+    rng = np.random.default_rng(77)
+    case = make_case(77, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                     page_size=16, q_lens=[0, 37, 0, 64, 0], kv_lens=[100, 250, 0, 0, 300],
+                     qkv_std=1 / np.sqrt(128), rng=rng)
+    O_ref, L_ref = oracle_attention(case)
+    out, lse = run_attn(DeviceCase(case))
+    assert_close(out, O_ref, dtype, lse, L_ref, what="empty sequences")
+
+
 # ------------------------------------------------------------------ tile classes ---------
 
 def tile_case_list():
