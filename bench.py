@@ -33,6 +33,7 @@ FP32_PEAK_TFLOPS = 157.3
 # Which roof binds each workload (algorithmic FLOP/byte against the 314.6 FLOP/B ridge).
 BOUND = {1: "hbm", 2: "hbm", 3: "mfma", 4: "mfma", 5: "hbm"}
 KERNEL_SOURCES = ["attn_bf16.hip", "combine.hip"]
+LAYERS = 32   # layers of the model step that is also timed as a captured graph
 
 
 def parse():
@@ -44,6 +45,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain copy kernel of known size")
+    p.add_argument("--no-graph", action="store_true", help="skip the captured 32-layer model step")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, then WRITE_SIZE) of `bench.py --calib-copy` into "
@@ -288,6 +290,45 @@ def main():
     torch.cuda.synchronize()
     attn_warm_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in attn_warm]))
 
+    # A model step of LAYERS layers (the tile mask built once, then each layer's attention
+    # call and KV commit; every layer reuses this workload's buffers, so it runs warm), issued
+    # call by call and replayed as one captured step graph, on the same side stream.
+    graph_rec = None
+    if not args.no_graph:
+        meta_u = bcp.StepMeta(**dc.meta_kwargs(), check=False)
+        gs = torch.cuda.Stream()
+
+        def model_step():
+            bcp.build_tile_mask(meta_u, tile_class=tile_class, phys_page=phys if nct else None, plan=plan)
+            for _ in range(LAYERS):
+                bcp.attn_block_causal_paged(meta_u, dc.q, dc.k_new, dc.v_new, k_cache, v_cache, out, plan=plan,
+                                            workspace=ws)
+                bcp.kv_commit_block(meta_u, dc.k_new, dc.v_new, dc.cu_q, dst, k_cache, v_cache, case.total_q)
+
+        n_rep = 5
+        with torch.cuda.stream(gs):
+            model_step()
+            ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ge[0].record(gs)
+            for _ in range(n_rep):
+                model_step()
+            ge[1].record(gs)
+            gs.synchronize()
+            eager_us = ge[0].elapsed_time(ge[1]) * 1e3 / n_rep
+            bcp.graph_begin(gs)
+            model_step()
+            graph = bcp.graph_end(gs)
+            graph.launch(gs)
+            ge[0].record(gs)
+            for _ in range(n_rep):
+                graph.launch(gs)
+            ge[1].record(gs)
+            gs.synchronize()
+            graph_us = ge[0].elapsed_time(ge[1]) * 1e3 / n_rep
+            graph.close()
+        graph_rec = {"layers": LAYERS, "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+                     "warm": True, "stream": "side stream, default priority"}
+
     if args.calib_copy:
         # A plain elementwise kernel (not the runtime's blit) that reads and writes 256 MiB.
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -344,6 +385,7 @@ def main():
         "kv_commit_us": round(float(np.mean(com_us)), 3),
         "kv_commit_gbps": round(2 * live_kv / (float(np.mean(com_us)) * 1e-6) / 1e9, 1),
         "warm_step_us": round(warm_step_us, 3),
+        "model_step_graph": graph_rec,
         "timed_wall_s_incl_flush": round(wall, 4),
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,

@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
   build_tile_mask(meta, tile_class=None, phys_page=None, plan=None)
   attn_block_causal_paged(meta, q, k_new, v_new, k_cache, v_cache, out, plan=None, ...)
   kv_commit_block(meta, k_src, v_src, cu_src, dst_start, k_cache, v_cache, total_commit, ...)
+  graph_begin(stream), graph_end(stream) -> Graph, Graph.launch(stream), Graph.close()
+    (bcp_graph_begin / _end / _launch / _destroy: capture a step's calls and replay them)
 """
 import ctypes
 import os
@@ -26,7 +28,8 @@ STATUS_NAMES = {0: "BCP_OK", 1: "BCP_E_ARG", 2: "BCP_E_UNSUPPORTED", 3: "BCP_E_R
 # Every function include/bcp.h declares.
 EXPORTED = ["bcp_num_q_tiles", "bcp_num_k_tiles", "bcp_plan_size", "build_tile_mask",
             "attn_block_causal_paged_workspace_size", "attn_block_causal_paged", "kv_commit_block",
-            "bcp_last_error", "bcp_abi_version"]
+            "bcp_last_error", "bcp_abi_version", "bcp_graph_begin", "bcp_graph_end", "bcp_graph_launch",
+            "bcp_graph_destroy"]
 
 
 class BcpError(RuntimeError):
@@ -84,6 +87,10 @@ def lib():
         L.attn_block_causal_paged.restype = ctypes.c_int
         L.kv_commit_block.argtypes = [P, VP, VP, VP, VP, VP, VP, I32, I32, VP, VP, VP, VP]
         L.kv_commit_block.restype = ctypes.c_int
+        L.bcp_graph_begin.argtypes, L.bcp_graph_begin.restype = [VP], ctypes.c_int
+        L.bcp_graph_end.argtypes, L.bcp_graph_end.restype = [VP, ctypes.POINTER(VP)], ctypes.c_int
+        L.bcp_graph_launch.argtypes, L.bcp_graph_launch.restype = [VP, VP], ctypes.c_int
+        L.bcp_graph_destroy.argtypes, L.bcp_graph_destroy.restype = [VP], None
         _lib = L
     return _lib
 
@@ -174,3 +181,45 @@ def kv_commit_block(meta, k_src, v_src, cu_src, dst_start, k_cache, v_cache, tot
                                  _ptr(dst_start), _ptr(src_blk), int(total_commit), int(n_src),
                                  _ptr(k_cache), _ptr(v_cache), _ptr(kv_blk_out),
                                  _stream(stream, k_cache)))
+
+
+def _graph_stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def graph_begin(stream=None):
+    """Start capturing the calls made on `stream` (not the legacy default stream)."""
+    _check(lib().bcp_graph_begin(_graph_stream(stream)))
+
+
+class Graph:
+    """A captured step (bcp_graph); launch() replays it, close() releases it."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise BcpError(BCP_E_ARG, "graph is closed")
+        _check(lib().bcp_graph_launch(self._h, _graph_stream(stream)))
+
+    def close(self):
+        if self._h:
+            lib().bcp_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def graph_end(stream=None):
+    """End the capture started by graph_begin on `stream`; returns the instantiated Graph."""
+    h = ctypes.c_void_p()
+    _check(lib().bcp_graph_end(_graph_stream(stream), ctypes.byref(h)))
+    return Graph(h.value)

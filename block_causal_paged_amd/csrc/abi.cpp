@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <new>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -13,6 +14,12 @@
 #include "bcp_internal.h"
 
 using namespace bcp;
+
+// A captured step: the HIP graph and its executable instance.
+struct bcp_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
 
 namespace {
 
@@ -104,8 +111,18 @@ int copy_to_host(std::vector<T>& v, const T* src, size_t n, hipStream_t stream) 
   return BCP_OK;
 }
 
+// Checked mode copies to the host, which a stream under capture cannot do.
+int refuse_if_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (st != hipStreamCaptureStatusNone) return fail(BCP_E_ARG, "checked mode cannot run on a stream under capture");
+  return BCP_OK;
+}
+
 // Checked mode: the metadata the kernels will read, validated on the host.
 int validate_metadata(const bcp_meta* m, hipStream_t stream) {
+  if (int rc = refuse_if_capturing(stream)) return rc;
   std::vector<int32_t> cu, kvl, pt, qb, kb;
   int rc;
   if ((rc = copy_to_host(cu, m->cu_q, m->batch + 1, stream))) return rc;
@@ -235,6 +252,51 @@ extern "C" {
 int bcp_abi_version(void) { return BCP_ABI_VERSION; }
 
 const char* bcp_last_error(void) { return g_err.c_str(); }
+
+int bcp_graph_begin(hipStream_t stream) {
+  hipError_t e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  g_err.clear();
+  return BCP_OK;
+}
+
+int bcp_graph_end(hipStream_t stream, bcp_graph** graph) {
+  if (!graph) return fail(BCP_E_ARG, "bcp_graph_end: graph is NULL");
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(stream, &g);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  bcp_graph* r = new (std::nothrow) bcp_graph{g, x};
+  if (!r) {
+    (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    return fail(BCP_E_ARG, "bcp_graph_end: out of host memory");
+  }
+  *graph = r;
+  g_err.clear();
+  return BCP_OK;
+}
+
+int bcp_graph_launch(bcp_graph* graph, hipStream_t stream) {
+  if (!graph) return fail(BCP_E_ARG, "bcp_graph_launch: graph is NULL");
+  hipError_t e = hipGraphLaunch(graph->exec, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  g_err.clear();
+  return BCP_OK;
+}
+
+void bcp_graph_destroy(bcp_graph* graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
+}
 
 int32_t bcp_num_q_tiles(const bcp_meta* m) {
   Geo g;
@@ -387,6 +449,7 @@ int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src, con
   if (m->flags & BCP_F_CHECK) {
     std::vector<int32_t> cu, rows, dst, pt;
     int rc;
+    if ((rc = refuse_if_capturing(stream))) return rc;
     if ((rc = copy_to_host(cu, cu_src, m->batch + 1, stream))) return rc;
     if ((rc = copy_to_host(dst, dst_start, m->batch, stream))) return rc;
     if ((rc = copy_to_host(pt, m->page_table, (size_t)m->batch * m->max_pages_per_seq, stream))) return rc;

@@ -24,7 +24,8 @@
  *   - Every pointer is a DEVICE pointer unless marked (host). All buffers are owned by
  *     the caller; the library allocates no device memory, keeps no pointer past a call
  *     and has no global state other than a thread-local error message and a per-device
- *     cache of the compute-unit count.
+ *     cache of the compute-unit count (the step-graph entry points below are the one
+ *     exception: a graph holds the HIP graph it captured until it is destroyed).
  *   - Work is enqueued asynchronously on `stream`; no entry point synchronizes, except
  *     in checked mode (BCP_F_CHECK), which copies the metadata to the host once and
  *     validates it before launching anything.
@@ -183,6 +184,32 @@ int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src,
                     const int32_t* cu_src, const int32_t* src_row, const int32_t* dst_start,
                     const int32_t* src_blk, int32_t total_commit, int32_t n_src,
                     void* k_cache, void* v_cache, int32_t* kv_blk_out, hipStream_t stream);
+
+/*
+ * Step graphs -- capture the calls a step makes on one stream and replay them
+ * ("Inference for Interpretable Text-Diffusion Models", section "Making CDE Fast", Compilation
+ * Strategy: fixed-shape decode graphs cut call latency; the Introspective Diffusion Language
+ * Models summary page, serving implementation and ablation: the extend forward is captured
+ * and replayed as a graph, the largest single gain in its system ablation).
+ *   bcp_graph_begin(stream)        starts capturing `stream` (thread-local capture mode); the
+ *                                  stream must not be the legacy default stream.
+ *   bcp_graph_end(stream, &graph)  ends the capture and instantiates it; *graph is owned by
+ *                                  the caller until bcp_graph_destroy.
+ *   bcp_graph_launch(graph, stream) enqueues one replay on `stream`.
+ *   bcp_graph_destroy(graph)       releases it (NULL is allowed).
+ * Between begin and end, entry points enqueue their kernels into the capture instead of
+ * running them; checked mode is refused there (BCP_E_ARG), since it copies to the host.
+ * A replay reads the current contents of every buffer the captured calls named, so those
+ * buffers must stay allocated, and the step's shapes (the host arguments) fixed, for as
+ * long as the graph is replayed. The HIP runtime may allocate memory to instantiate a
+ * graph; these are the only entry points that keep state past a call.
+ * Errors: BCP_E_ARG (NULL graph pointer), BCP_E_HIP (the HIP graph call failed).
+ */
+typedef struct bcp_graph bcp_graph;
+int bcp_graph_begin(hipStream_t stream);
+int bcp_graph_end(hipStream_t stream, bcp_graph** graph);
+int bcp_graph_launch(bcp_graph* graph, hipStream_t stream);
+void bcp_graph_destroy(bcp_graph* graph);
 
 /* Thread-local description of the last non-OK return on this thread (host string). */
 const char* bcp_last_error(void);

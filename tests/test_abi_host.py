@@ -121,6 +121,19 @@ def test_commit_rejects():
     assert commit(meta(), total=0) == bcp.BCP_OK                              # nothing to do
 
 
+def test_graph_entry_points_reject_null_handles():
+    # Host-side checks only: no capture is started, so no GPU is needed.
+    L = bcp.lib()
+    assert L.bcp_graph_end(None, None) == bcp.BCP_E_ARG
+    assert b"NULL" in L.bcp_last_error()
+    assert L.bcp_graph_launch(None, None) == bcp.BCP_E_ARG
+    L.bcp_graph_destroy(None)   # a no-op
+    g = bcp.Graph(None)
+    with pytest.raises(bcp.BcpError):
+        g.launch(0)
+    g.close()
+
+
 def test_error_message_is_thread_local_and_specific():
     attn(meta(head_dim=96))
     assert b"head_dim 96" in bcp.lib().bcp_last_error()
