@@ -8,7 +8,8 @@ the active blocks, and
     S = scale * q_h . K_g^T,   S = -inf where the block-causal mask forbids the pair,
     m = max_j S,  w = exp(S - m),  l = sum_j w,  O = (w . V_g) / l,  LSE = m + ln l.
 
-The mask is mask.dense_mask (sections cited there); the gather is paging.gather. A row
+The mask is mask.dense_mask (sections cited there, including the optional sliding
+window); the gather is paging.gather. A row
 with no visible key (impossible on valid input, since every row sees itself) gets O = 0
 and LSE = -inf. The default scale is 1/sqrt(head_dim): the pages never state a scale,
 and this is the usual one.
@@ -22,7 +23,7 @@ from .paging import translate
 
 def attention_rows(q, k_new, v_new, k_cache, v_cache, cu_q, kv_len, page_table, page_size,
                    num_pages, s, rows=None, block_size=None, scale=None, q_blk=None, kv_blk=None,
-                   row_chunk=512):
+                   row_chunk=512, window=None, q_pos=None, kv_pos=None):
     """O [len(rows), Hq, d] and LSE [len(rows), Hq] (float64) for local live rows of sequence s."""
     Hq, d = q.shape[1], q.shape[2]
     Hkv = k_new.shape[1]
@@ -39,9 +40,14 @@ def attention_rows(q, k_new, v_new, k_cache, v_cache, cu_q, kv_len, page_table, 
     Vf = np.concatenate([widen(v_cache[page, slot]), widen(v_new[lo:hi])], axis=0)
     if q_blk is not None:
         kb = np.asarray(kv_blk).reshape(-1)[page * int(page_size) + slot]
-        M_all = dense_mask(q_len, n_cached, q_blk=np.asarray(q_blk)[lo:hi], kv_blk=kb)
+        qp = kp = None
+        if window:
+            qp = np.asarray(q_pos)[lo:hi]
+            kp = np.asarray(kv_pos).reshape(-1)[page * int(page_size) + slot]
+        M_all = dense_mask(q_len, n_cached, q_blk=np.asarray(q_blk)[lo:hi], kv_blk=kb, window=window,
+                           q_pos=qp, kv_pos=kp)
     else:
-        M_all = dense_mask(q_len, n_cached, block_size=block_size)
+        M_all = dense_mask(q_len, n_cached, block_size=block_size, window=window)
 
     O = np.zeros((rows.size, Hq, d), dtype=np.float64)
     L = np.full((rows.size, Hq), -np.inf, dtype=np.float64)
@@ -68,7 +74,8 @@ def attention_rows(q, k_new, v_new, k_cache, v_cache, cu_q, kv_len, page_table, 
 
 
 def attention(q, k_new, v_new, k_cache, v_cache, cu_q, kv_len, page_table, page_size, num_pages,
-              block_size=None, scale=None, q_blk=None, kv_blk=None, rows=None):
+              block_size=None, scale=None, q_blk=None, kv_blk=None, rows=None, window=None,
+              q_pos=None, kv_pos=None):
     """O [total_q, Hq, d], LSE [total_q, Hq] in float64 for every sequence.
 
     rows: optional {s: local row indices} to compute a sample; other rows stay NaN.
@@ -83,7 +90,8 @@ def attention(q, k_new, v_new, k_cache, v_cache, cu_q, kv_len, page_table, page_
         r = None if rows is None else np.asarray(rows[s], dtype=np.int64)
         Os, Ls = attention_rows(q, k_new, v_new, k_cache, v_cache, cu_q, kv_len, page_table,
                                 page_size, num_pages, s, rows=r, block_size=block_size,
-                                scale=scale, q_blk=q_blk, kv_blk=kv_blk)
+                                scale=scale, q_blk=q_blk, kv_blk=kv_blk, window=window, q_pos=q_pos,
+                                kv_pos=kv_pos)
         idx = int(cu_q[s]) + (np.arange(int(cu_q[s + 1]) - int(cu_q[s])) if r is None else r)
         O[idx] = Os
         L[idx] = Ls

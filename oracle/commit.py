@@ -6,7 +6,8 @@ unmasked a final pass commits its keys and values to the cache. The cache is pag
 (section "Paged Attention"), so logical destination row j of sequence s is page
 page_table[s, j // P], slot j % P. Entries in the multi-canvas arena also record their
 position tag beside the key and value ("Inference: Fewer, smaller forwards",
-Advancement 11); here that tag is the block id.
+Advancement 11); here the tags are the block id and, for sliding-window layers, the
+absolute position, each copied from its source row.
 
 The copy is bitwise: every byte outside the destination slots keeps its old value. Two
 rows landing on the same slot is an error (the result would depend on write order).
@@ -26,8 +27,9 @@ def _as_bits(a):
 
 
 def commit(k_cache, v_cache, k_src, v_src, cu_src, dst_start, page_table, page_size, num_pages,
-           src_row=None, kv_blk=None, src_blk=None):
-    """Return (k_cache', v_cache', kv_blk') after committing rows; inputs are not modified.
+           src_row=None, kv_blk=None, src_blk=None, kv_pos=None, src_pos=None):
+    """Return (k_cache', v_cache', kv_blk') -- and kv_pos' as a fourth item when kv_pos is
+    given -- after committing rows; inputs are not modified.
 
     For sequence s and r < cu_src[s+1]-cu_src[s]: source row = src_row[cu_src[s]+r]
     (identity when src_row is None) goes to logical row dst_start[s] + r.
@@ -37,6 +39,9 @@ def commit(k_cache, v_cache, k_src, v_src, cu_src, dst_start, page_table, page_s
     kb = None if kv_blk is None else np.asarray(kv_blk, dtype=np.int32).reshape(-1).copy()
     if src_blk is not None and kb is None:
         raise ValueError("src_blk given without kv_blk")
+    kp = None if kv_pos is None else np.asarray(kv_pos, dtype=np.int32).reshape(-1).copy()
+    if src_pos is not None and kp is None:
+        raise ValueError("src_pos given without kv_pos")
     P = int(page_size)
     batch = len(cu_src) - 1
     seen = set()
@@ -61,6 +66,10 @@ def commit(k_cache, v_cache, k_src, v_src, cu_src, dst_start, page_table, page_s
             vc[key] = vs[row]
             if src_blk is not None:
                 kb[key[0] * P + key[1]] = int(src_blk[row])
+            if src_pos is not None:
+                kp[key[0] * P + key[1]] = int(src_pos[row])
     if np.asarray(k_cache).dtype == np.float32:
         kc, vc = kc.view(np.float32), vc.view(np.float32)
+    if kv_pos is not None:
+        return kc, vc, kb, kp
     return kc, vc, kb

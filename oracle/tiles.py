@@ -26,7 +26,8 @@ def _ceil_div(a, b):
 
 
 def tile_classes(cu_q, kv_len, tile_q, tile_k, max_q_len, max_kv_len, block_size=None,
-                 q_blk=None, kv_blk=None, page_table=None, page_size=None, num_pages=None):
+                 q_blk=None, kv_blk=None, page_table=None, page_size=None, num_pages=None,
+                 window=None, q_pos=None, kv_pos=None):
     """uint8 [batch, nqt, nct + nlt] of TILE_* codes."""
     batch = len(cu_q) - 1
     tq, tk = int(tile_q), int(tile_k)
@@ -39,9 +40,14 @@ def tile_classes(cu_q, kv_len, tile_q, tile_k, max_q_len, max_kv_len, block_size
         if q_blk is not None:
             page, slot = translate(page_table, kv_len, page_size, num_pages, s)
             kb = np.asarray(kv_blk).reshape(-1)[page * int(page_size) + slot]
-            M = dense_mask(q_len, n_cached, q_blk=np.asarray(q_blk)[lo:hi], kv_blk=kb)
+            qp = kp = None
+            if window:
+                qp = np.asarray(q_pos)[lo:hi]
+                kp = np.asarray(kv_pos).reshape(-1)[page * int(page_size) + slot]
+            M = dense_mask(q_len, n_cached, q_blk=np.asarray(q_blk)[lo:hi], kv_blk=kb, window=window,
+                           q_pos=qp, kv_pos=kp)
         else:
-            M = dense_mask(q_len, n_cached, block_size=block_size)
+            M = dense_mask(q_len, n_cached, block_size=block_size, window=window)
         # Pad each region's columns with "not visible" out to its whole tile grid.
         cached = np.zeros((q_len, nct * tk), dtype=bool)
         cached[:, :n_cached] = M[:, :n_cached]

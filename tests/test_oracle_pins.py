@@ -508,3 +508,136 @@ def test_workload_shapes():
     assert c1.kv_len.tolist() == [48] and c1.q_lens.tolist() == [16]
     assert c1.page_table.tolist() == [[0, 1, 2, 3]] and c1.dtype == "f32"
     assert np.isnan(c1.k_cache[3]).all() and not np.isnan(c1.k_cache[:3]).any()
+
+
+# ---------------------------------------------------------------- sliding window ----
+# "Inference: Fewer, smaller forwards", Advancement 11: arena entries keep their absolute
+# position, so a sliding-window layer can band-mask entries outside the window. Reading:
+# a key at position pk is visible to a query at position pq only if pq - pk < W (and the
+# block rule allows it); keys at later positions are never cut by the window.
+
+def test_window_one_with_token_blocks_sees_only_itself():
+    """W = 1, D = 1, empty cache: each row's only visible key is its own, so O = v_i and
+    LSE = scale * q_i . k_i exactly (softmax over one key)."""
+    rng = np.random.default_rng(71)
+    c, _ = contiguous_case(rng, q_len=11, kv_len=0, Hq=2, Hkv=2, d=8, D=1, P=4)
+    O, L = run(c, window=1)
+    np.testing.assert_allclose(O, c["v_new"].astype(np.float64), rtol=0, atol=1e-15)
+    lse = (c["q"].astype(np.float64) * c["k_new"].astype(np.float64)).sum(-1) / math.sqrt(8)
+    np.testing.assert_allclose(L, lse, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("W", [1, 3, 7, 40])
+def test_token_causal_window_equals_sdpa_on_key_slices(W):
+    """D = 1 with a window: row i attends to keys max(0, i-W+1) .. i, which torch SDPA
+    (float64, no mask) computes on that slice of the keys, row by row."""
+    rng = np.random.default_rng(72)
+    c, _ = contiguous_case(rng, q_len=23, kv_len=0, Hq=2, Hkv=1, d=8, D=1, P=4)
+    O, _ = run(c, window=W)
+    k, v = expand_gqa(c["k_new"], 2), expand_gqa(c["v_new"], 2)
+    for i in range(23):
+        a = max(0, i - W + 1)
+        ref = sdpa64(c["q"][i:i + 1], k[a:i + 1], v[a:i + 1])
+        np.testing.assert_allclose(O[i:i + 1], ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [5, 30, 61])
+def test_window_over_cache_equals_sdpa_on_position_slices(W):
+    """One bidirectional block (D >= q_len) over a cache: row i at position kv_len + i sees
+    the contiguous positions from kv_len + i - W + 1 on (cached then live), i.e. SDPA over
+    that slice of the concatenated [cached; live] keys."""
+    rng = np.random.default_rng(73)
+    q_len, kv_len = 16, 45
+    c, (Kc, Vc) = contiguous_case(rng, q_len=q_len, kv_len=kv_len, Hq=4, Hkv=2, d=16, D=16, P=8)
+    O, _ = run(c, window=W)
+    K = expand_gqa(np.concatenate([Kc, c["k_new"]]), 2)
+    V = expand_gqa(np.concatenate([Vc, c["v_new"]]), 2)
+    for i in range(q_len):
+        a = max(0, kv_len + i - W + 1)
+        np.testing.assert_allclose(O[i:i + 1], sdpa64(c["q"][i:i + 1], K[a:], V[a:]), atol=1e-12)
+
+
+def test_window_wider_than_the_sequence_changes_nothing():
+    rng = np.random.default_rng(74)
+    c, _ = contiguous_case(rng, q_len=20, kv_len=33, Hq=4, Hkv=2, d=8, D=4, P=8)
+    O0, L0 = run(c)
+    O1, L1 = run(c, window=20 + 33)
+    np.testing.assert_array_equal(O0, O1)
+    np.testing.assert_array_equal(L0, L1)
+
+
+def test_mode_B_positions_in_row_order_equal_mode_A_window():
+    """Mode B with block ids and positions laid out as mode A has them implicitly
+    (committed row j at position j and block -1; live row i at kv_len + i, block i // D)
+    gives the same result as mode A with the same window."""
+    rng = np.random.default_rng(75)
+    q_len, kv_len, D, P, W = 19, 27, 4, 8, 9
+    c, _ = contiguous_case(rng, q_len=q_len, kv_len=kv_len, Hq=2, Hkv=1, d=8, D=D, P=P)
+    pt = c["page_table"][0]
+    kv_blk = np.full(c["num_pages"] * P, 99, np.int32)
+    kv_pos = np.full(c["num_pages"] * P, -10 ** 6, np.int32)
+    for j in range(kv_len):
+        kv_blk[pt[j // P] * P + j % P] = -1
+        kv_pos[pt[j // P] * P + j % P] = j
+    q_blk = (np.arange(q_len) // D).astype(np.int32)
+    q_pos = (kv_len + np.arange(q_len)).astype(np.int32)
+    OA, LA = run(c, window=W)
+    OB, LB = run(c, window=W, q_blk=q_blk, kv_blk=kv_blk, q_pos=q_pos, kv_pos=kv_pos)
+    np.testing.assert_array_equal(OA, OB)
+    np.testing.assert_array_equal(LA, LB)
+
+
+def _window_class_mode_A(i0, i1, j0, nvalid, tk, kvl, D, W, cached):
+    """Class of a mode-A tile with a window, from interval bounds (rows i0..i1-1 of the
+    q-tile, keys j0..j0+nvalid-1 of the region): for row i the visible keys form the
+    interval [lo(i), hi(i)], both bounds non-decreasing in i."""
+    if i1 <= i0 or nvalid <= 0:
+        return TILE_SKIP
+    jl = j0 + nvalid - 1
+    if cached:   # position j; every committed row passes the block rule
+        lo = lambda i: max(j0, kvl + i - W + 1)
+        hi = lambda i: jl
+    else:        # position kv_len + j; block rule j // D <= i // D
+        lo = lambda i: max(j0, i - W + 1)
+        hi = lambda i: min(jl, (i // D + 1) * D - 1)
+    seen = [lo(i) <= hi(i) for i in range(i0, i1)]
+    full = nvalid == tk and all(lo(i) == j0 and hi(i) == jl for i in range(i0, i1))
+    return TILE_FULL if full else (TILE_PARTIAL if any(seen) else TILE_SKIP)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_window_tiles_brute_force_equals_interval_rule(seed):
+    """Mode-A tile classes with a window, read off the dense mask, equal the per-row
+    interval rule above (which the kernels' classifier follows in closed form)."""
+    rng = np.random.default_rng(200 + seed)
+    B = 3
+    q_lens = rng.integers(0, 70, B)
+    kv_lens = rng.integers(0, 90, B)
+    tq, tk, P, D, W = [(8, 8, 4, 3, 5), (16, 8, 8, 4, 17), (4, 16, 4, 1, 9), (32, 16, 16, 8, 40)][seed]
+    c = make_case(seed, dtype="f32", num_q_heads=1, num_kv_heads=1, head_dim=4, block_size=D,
+                  page_size=P, q_lens=q_lens, kv_lens=kv_lens, rng=rng)
+    got = oracle.tile_classes(c.cu_q, c.kv_len, tq, tk, c.max_q_len, c.max_kv_len, block_size=D, window=W)
+    nct = -(-c.max_kv_len // tk)
+    for s in range(B):
+        for r in range(got.shape[1]):
+            i0, i1 = r * tq, min((r + 1) * tq, int(q_lens[s]))
+            for t in range(got.shape[2]):
+                cached = t < nct
+                j0 = (t if cached else t - nct) * tk
+                n = max(0, min(tk, (int(kv_lens[s]) if cached else int(q_lens[s])) - j0))
+                assert got[s, r, t] == _window_class_mode_A(i0, i1, j0, n, tk, int(kv_lens[s]), D, W, cached)
+
+
+def test_commit_copies_position_tags():
+    """Commit writes each row's position beside its block id, at the row's slot only."""
+    g = GOLD["hand_commit"]
+    P = g["page_size"]
+    src = np.arange(1, 4, dtype=np.float32).reshape(3, 1, 1)
+    pool = np.zeros((6, P, 1, 1), np.float32)
+    kc, _, kvb, kvp = oracle.commit(pool, pool, src, src, [0, 3], [g["dst_start"]],
+                                    np.array([g["page_table"]], np.int32), P, 6,
+                                    kv_blk=np.full(12, -1, np.int32), src_blk=np.array([7, 8, 9]),
+                                    kv_pos=np.full(12, -1, np.int32), src_pos=np.array([40, 41, 42]))
+    for r, (page, slot) in enumerate(g["slots"]):
+        assert kvp[page * P + slot] == 40 + r
+    assert np.count_nonzero(kvp >= 0) == 3
