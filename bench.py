@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain copy kernel of known size")
     p.add_argument("--no-graph", action="store_true", help="skip the captured 32-layer model step")
+    p.add_argument("--window", type=int, default=0,
+                   help="sliding window in positions (mode A workloads; 0 = none)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, then WRITE_SIZE) of `bench.py --calib-copy` into "
@@ -116,17 +118,29 @@ def summarize_traffic(args):
     print(json.dumps(rec))
 
 
-def workload_stats(case):
-    """Useful FLOPs (4*d per visible (row, key, query head)) and algorithmic bytes."""
+def workload_stats(case, window=0):
+    """Useful FLOPs (4*d per visible (row, key, query head)) and algorithmic bytes.
+
+    With a sliding window W (mode A), live row i sits at position kv_len + i and sees the
+    committed rows j > kv_len + i - W and the live rows j > i - W of its block or earlier
+    ones; only the committed rows that some live row sees (the last W - 1) count as bytes.
+    """
     import numpy as np
     d, Hq, Hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
     esize = 2 if case.dtype == "bf16" else 4
     visible = 0
+    cached_rows = 0
     for s in range(case.batch):
         ql, kl = int(case.q_lens[s]), int(case.kv_len[s])
+        cached_rows += kl if not window else min(kl, window - 1)
         if case.q_blk is None:
             i = np.arange(ql)
             live = np.minimum(ql, (i // case.block_size + 1) * case.block_size)
+            if window:
+                cached = np.clip(window - 1 - i, 0, kl)
+                live = live - np.maximum(0, i - window + 1)
+                visible += int((cached + live).sum())
+                continue
             visible += int((kl + live).sum())
         else:
             qb = np.sort(case.q_blk_seqs[s])
@@ -135,7 +149,7 @@ def workload_stats(case):
             visible += int(np.searchsorted(kb, rows, side="right").sum()
                            + np.searchsorted(qb, rows, side="right").sum())
     flops = 4.0 * d * Hq * visible
-    cached_kv = float(case.kv_len.sum()) * Hkv * d * esize * 2
+    cached_kv = float(cached_rows) * Hkv * d * esize * 2
     live_kv = float(case.total_q) * Hkv * d * esize * 2
     q_o = float(case.total_q) * Hq * d * esize * 2
     return flops, cached_kv, live_kv, q_o
@@ -165,7 +179,7 @@ def traffic_from_profile(cfg):
     return rec.get("hbm_bytes_per_call")
 
 
-def cpu_baseline(case, budget_s):
+def cpu_baseline(case, budget_s, window=0):
     """The oracle as it stands, over whole sequences of the same workload in order, pass
     after pass, until the budget is spent; scaled to microseconds per full step by the
     number of query rows covered."""
@@ -181,7 +195,8 @@ def cpu_baseline(case, budget_s):
         s = seqs % case.batch
         oracle.attention_rows(case.q, case.k_new, case.v_new, case.k_cache, case.v_cache, case.cu_q,
                               case.kv_len, case.page_table, case.page_size, case.num_pages, s,
-                              block_size=case.block_size, q_blk=case.q_blk, kv_blk=case.kv_blk)
+                              block_size=case.block_size, q_blk=case.q_blk, kv_blk=case.kv_blk,
+                              window=window or None)
         rows_done += int(case.q_lens[s])
         seqs += 1
         if time.perf_counter() - t0 > budget_s:
@@ -217,7 +232,10 @@ def main():
     case = config(cfg)
     dc = DeviceCase(case)
     torch.cuda.synchronize()
-    meta = bcp.StepMeta(**dc.meta_kwargs())
+    if args.window and case.q_blk is not None:
+        print("--window applies to mode A workloads only", file=sys.stderr)
+        sys.exit(2)
+    meta = bcp.StepMeta(**dc.meta_kwargs(), window=args.window)
     plan = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda")
     nqt, nkt = bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
     tile_class = torch.empty((case.batch, nqt, nkt), dtype=torch.uint8, device="cuda")
@@ -295,7 +313,7 @@ def main():
     # call by call and replayed as one captured step graph, on the same side stream.
     graph_rec = None
     if not args.no_graph:
-        meta_u = bcp.StepMeta(**dc.meta_kwargs(), check=False)
+        meta_u = bcp.StepMeta(**dc.meta_kwargs(), check=False, window=args.window)
         gs = torch.cuda.Stream()
 
         def model_step():
@@ -337,7 +355,7 @@ def main():
             torch.mul(src, 1.0, out=dst_buf)
         torch.cuda.synchronize()
 
-    flops, cached_kv, live_kv, q_o = workload_stats(case)
+    flops, cached_kv, live_kv, q_o = workload_stats(case, args.window)
     algo_bytes = cached_kv + live_kv + q_o
     a_med = float(np.median(attn_us))
     a_mean = float(np.mean(attn_us))
@@ -347,7 +365,7 @@ def main():
     else:
         peak = MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else FP32_PEAK_TFLOPS
         achieved, unit = flops / (a_mean * 1e-6) / 1e12, "TFLOP/s"
-    traffic = traffic_from_profile(cfg)
+    traffic = None if args.window else traffic_from_profile(cfg)
 
     rec = {
         "metric": METRIC,
@@ -366,7 +384,8 @@ def main():
                    "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
                    "total_q": case.total_q, "kv_len_mean": float(case.kv_len.mean()),
                    "kv_len_max": int(case.kv_len.max()), "page_size": case.page_size,
-                   "block_size": case.block_size, "mode": case.mode},
+                   "block_size": case.block_size, "mode": case.mode,
+                   **({"window": args.window} if args.window else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
                      "traffic": traffic,
@@ -391,7 +410,7 @@ def main():
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, args.window)
     print(json.dumps(rec))
 
 

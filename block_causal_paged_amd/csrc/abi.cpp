@@ -76,6 +76,9 @@ int check_meta(const bcp_meta* m, Geo* g) {
     return fail(BCP_E_ARG, "max_kv_len %d exceeds max_pages_per_seq * page_size", m->max_kv_len);
   if ((int64_t)m->num_pages * m->page_size > INT32_MAX || (int64_t)m->batch * m->max_pages_per_seq > INT32_MAX)
     return fail(BCP_E_ARG, "pool or page table too large for 32-bit slot indices");
+  if (m->window < 0) return fail(BCP_E_ARG, "window must be >= 0 (got %d)", m->window);
+  if (m->window > 0 && m->q_blk)
+    return fail(BCP_E_UNSUPPORTED, "a sliding window is supported in mode A only");
   g->G = m->num_q_heads / m->num_kv_heads;
   g->mode_b = m->q_blk != nullptr;
   g->tq = m->tile_q ? m->tile_q : std::max(1, kRowsPerWG / g->G);
@@ -213,6 +216,7 @@ ClassifyArgs classify_args(const bcp_meta* m, const Geo& g) {
   a.phys_per_tile = std::max(1, g.tk / m->page_size);
   a.phys_tiles = g.nct;
   a.num_kv_heads = m->num_kv_heads;
+  a.window = g.mode_b ? 0 : m->window;
   return a;
 }
 
@@ -409,6 +413,7 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   a.mode_b = g.mode_b;
   a.max_items = plan_layout(m->batch, g.nqt, g.nkt, m->num_kv_heads).max_items;
   a.page_shift = (m->page_size & (m->page_size - 1)) ? -1 : __builtin_ctz((unsigned)m->page_size);
+  a.window = g.mode_b ? 0 : m->window;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)m->head_dim);
   a.scale_log2 = sc * 1.4426950408889634f;
 

@@ -561,6 +561,19 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
               for (int c = 0; c < 4; ++c)
                 if (kbw[c] > qblk) sc[kb][4 * v4 + c] = -INFINITY;
             }
+          if (a.window > 0) {
+            // Sliding window (mode A): the key in column cc of the tile lies wbase - cc
+            // positions before this lane's query (committed row j at position j, live row
+            // i at kv_len + i); it drops out once that distance reaches the window.
+            const int vt = e_t >> 1;
+            const int wbase = pos + (vt < a.nct ? it.kvl - vt * kTileK : -(vt - a.nct) * kTileK);
+            const int thr = wbase - a.window - 4 * hl;   // mask 32kb + 8(v/4) + v%4 <= thr
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v)
+                if (32 * kb + 8 * (v / 4) + v % 4 <= thr) sc[kb][v] = -INFINITY;
+          }
         }
         // Online softmax in the log2 domain, with a lazy reference max: m only moves when
         // a row's max grows by more than 2^8 (or on its first visible key). Numerator and

@@ -96,6 +96,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       }
       __syncthreads();
 
+      // Sliding window (mode A): key k of the tile lies wbase - k positions before this
+      // row's query (committed row j at position j, live row i at kv_len + i).
+      const int wbase = pos + (vt < a.nct ? kvl - vt * kTileK : -(vt - a.nct) * kTileK);
+      const bool band = partial && a.window > 0;
       float sc[kTileK];
       float mx = -INFINITY;
 #pragma unroll
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
           acc = fmaf(qv[d + 3], kk[3], acc);
         }
         if (partial && kblk[k] > qblk) acc = -INFINITY;
+        if (band && wbase - k >= a.window) acc = -INFINITY;
         sc[k] = acc;
         mx = fmaxf(mx, acc);
       }

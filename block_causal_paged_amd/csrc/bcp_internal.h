@@ -87,6 +87,7 @@ struct ClassifyArgs {
   int batch, total_q, tile_q, tile_k, nqt, nct, nkt, block_size, page_size, num_pages,
       max_pages, max_q_len, mode_b, phys_per_tile, phys_tiles, num_kv_heads;
   int grid_q;             // q-tile workgroups per sequence: max(nqt, 1)
+  int window;             // sliding window in positions (mode A), 0 for none
 };
 
 struct PlanArgs {
@@ -117,6 +118,7 @@ struct AttnArgs {
   int batch, total_q, max_q_len, Hq, Hkv, G, tile_q, nqt, nkt, nct, page_size, num_pages,
       max_pages, block_size, mode_b, max_items;
   int page_shift;         // log2(page_size) when it is a power of two, else -1
+  int window;             // sliding window in positions (mode A), 0 for none
   float scale_log2;       // softmax scale times log2(e)
 };
 

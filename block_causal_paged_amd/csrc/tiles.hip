@@ -199,6 +199,25 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
       if (nvalid == 0 || kmin > qmax) cls = BCP_TILE_SKIP;
       else if (kmax <= qmin && nvalid == a.tile_k) cls = BCP_TILE_FULL;
       else cls = BCP_TILE_PARTIAL;
+      if (a.window > 0 && cls != BCP_TILE_SKIP) {
+        // Sliding window (mode A): query row i sits at position kvl + i, committed key j at
+        // j and live key j at kvl + j; a key is in the band while the query is fewer than
+        // W positions past it. Rows i0..i1-1 against keys lo..hi of the tile:
+        const int lo = (t < a.nct ? t : t - a.nct) * a.tile_k, hi = lo + nvalid - 1;
+        const int64_t d_near = (t < a.nct ? (int64_t)kvl : 0) + i0 - hi;       // smallest distance
+        const int64_t d_far = (t < a.nct ? (int64_t)kvl : 0) + (i1 - 1) - lo;  // largest distance
+        if (t < a.nct) {
+          if (d_near >= a.window) cls = BCP_TILE_SKIP;
+          else if (d_far >= a.window) cls = BCP_TILE_PARTIAL;
+        } else {
+          // Key j is seen by the rows of its own block onwards, up to row j + W - 1; over
+          // the tile's keys these row sets join into one interval.
+          const int first = (lo / a.block_size) * a.block_size;
+          const int64_t last = (int64_t)hi + a.window - 1;
+          if (max(i0, first) > min((int64_t)i1 - 1, last)) cls = BCP_TILE_SKIP;
+          else if (d_far >= a.window) cls = BCP_TILE_PARTIAL;
+        }
+      }
     }
     if (t < a.nkt && a.tile_class) a.tile_class[list_base + t] = (uint8_t)cls;
     if (a.plan) {

@@ -14,7 +14,9 @@
  *             causal across blocks, never to later blocks);
  *     mode B: to committed row j iff kv_blk[slot(j)] <= q_blk[i], and to live row j iff
  *             q_blk[j] <= q_blk[i] (block ids per row, as in multi-canvas decoding where
- *             canvas c sees the prompt, earlier canvases and itself).
+ *             canvas c sees the prompt, earlier canvases and itself);
+ *   with a sliding window W (mode A), additionally only to keys at most W-1 positions
+ *   before the query (committed row j at position j, live row i at kv_len + i).
  *   out = softmax(scale * q k^T restricted to visible keys) v, per query head, with
  *   grouped-query attention: query head h reads kv head h / (Hq / Hkv).
  *   When a block is finished its rows are committed: copied bit for bit into the page
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BCP_ABI_VERSION 1
+#define BCP_ABI_VERSION 2
 
 enum { BCP_BF16 = 0, BCP_F32 = 1 };
 enum { BCP_TILE_SKIP = 0, BCP_TILE_PARTIAL = 1, BCP_TILE_FULL = 2 };
@@ -96,6 +98,11 @@ typedef struct bcp_meta {
   int32_t tile_q;              /* query positions per q-tile; 0 -> 256/(Hq/Hkv) */
   int32_t tile_k;              /* keys per k-tile; 0 -> 64 */
   uint32_t flags;              /* BCP_F_CHECK */
+  int32_t window;              /* sliding window W >= 1 in positions, or 0 for none (mode A only):
+                                  key position pk stays visible to query position pq only if
+                                  pq - pk < W, committed row j at position j and live row i at
+                                  kv_len + i ("Inference: Fewer, smaller forwards", Advancement
+                                  11); tiles entirely outside the window are SKIP */
 } bcp_meta;
 
 /* Number of query tiles / key tiles of the step's tile grid (after the tile defaults).

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_function():
     assert set(decl) == set(bcp.EXPORTED), decl
     for name in decl:
         assert hasattr(L, name), name
-    assert L.bcp_abi_version() == 1
+    assert L.bcp_abi_version() == 2
 
 
 def meta(**over):
@@ -76,6 +76,8 @@ def test_geometry_queries():
     (dict(num_q_heads=24), bcp.BCP_E_UNSUPPORTED),        # 3 query heads per kv head
     (dict(tile_q=32), bcp.BCP_E_UNSUPPORTED),
     (dict(tile_k=32), bcp.BCP_E_UNSUPPORTED),
+    (dict(window=-1), bcp.BCP_E_ARG),
+    (dict(window=256, q_blk=FAKE, kv_blk=FAKE), bcp.BCP_E_UNSUPPORTED),   # window in mode B
 ])
 def test_attention_rejects_bad_meta(over, code):
     assert attn(meta(**over)) == code

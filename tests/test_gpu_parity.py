@@ -289,10 +289,10 @@ def test_tile_classes_page_figures(name, spec, tq, tk):
     check_tiles(case, tq, tk)
 
 
-def check_tiles(case, tq, tk, with_plan=False):
+def check_tiles(case, tq, tk, with_plan=False, window=0):
     # With a plan requested too, the classes and pages must be the same.
     dc = DeviceCase(case)
-    meta = bcp.StepMeta(**dc.meta_kwargs(), tile_q=tq, tile_k=tk, check=True)
+    meta = bcp.StepMeta(**dc.meta_kwargs(), tile_q=tq, tile_k=tk, check=True, window=window)
     nqt, nkt = bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
     nct = -(-case.max_kv_len // tk)
     ppt = max(1, tk // case.page_size)
@@ -301,7 +301,7 @@ def check_tiles(case, tq, tk, with_plan=False):
     plan_t = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda") if with_plan else None
     bcp.build_tile_mask(meta, tile_class=tc, phys_page=pp, plan=plan_t)
     torch.cuda.synchronize()
-    ref = oracle_tiles(case, tq, tk)
+    ref = oracle_tiles(case, tq, tk, window=window or None)
     got = tc.cpu().numpy()
     assert got.shape == ref.shape
     np.testing.assert_array_equal(got, ref)
@@ -329,6 +329,78 @@ def test_tile_classes_workloads(workloads, n):
     got = check_tiles(case, 64, 64)
     if n == 3:
         assert (got == bcp.BCP_TILE_FULL).sum() == 4 * 8256 and (got == bcp.BCP_TILE_PARTIAL).sum() == 0
+
+
+# ------------------------------------------------------------------ sliding window -------
+# Mode A with a band of W positions (committed row j at position j, live row i at
+# kv_len + i): tiles wholly outside the band are SKIP, tiles it cuts are PARTIAL.
+
+WINDOW_TILES = [(41, 64, 64, 16, 1), (42, 64, 64, 16, 37), (43, 16, 32, 8, 64), (44, 128, 64, 64, 200),
+                (45, 7, 5, 3, 9), (46, 64, 64, 16, 100000)]
+
+
+@pytest.mark.parametrize("seed,tq,tk,P,W", WINDOW_TILES)
+def test_window_tile_classes(seed, tq, tk, P, W):
+    case = small_case(seed, G=4, d=64, D=5, P=P, max_q=150, max_kv=400)
+    got = check_tiles(case, tq, tk, window=W)
+    if (tq, tk) == (64, 64):
+        check_tiles(case, tq, tk, with_plan=True, window=W)
+    if W == 100000:   # a band wider than any sequence changes no class
+        np.testing.assert_array_equal(got, oracle_tiles(case, tq, tk))
+
+
+WINDOW_SMALL = [
+    dict(seed=51, dtype="bf16", G=4, d=128, D=16, P=16, W=1),
+    dict(seed=52, dtype="bf16", G=4, d=128, D=16, P=16, W=23),
+    dict(seed=53, dtype="bf16", G=2, d=64, D=3, P=16, W=64),
+    dict(seed=54, dtype="bf16", G=8, d=128, D=64, P=64, W=130),
+    dict(seed=55, dtype="bf16", G=4, d=64, D=1, P=8, W=5),
+    dict(seed=56, dtype="bf16", G=4, d=128, D=64, P=64, W=257, batch=5, max_q=300, max_kv=700),
+    dict(seed=57, dtype="f32", G=4, d=128, D=16, P=16, W=40),
+    dict(seed=58, dtype="f32", G=2, d=64, D=5, P=8, W=3),
+]
+
+
+@pytest.mark.parametrize("spec", WINDOW_SMALL, ids=lambda s: "-".join(f"{k}{v}" for k, v in s.items()))
+def test_window_attention_small(spec):
+    spec = dict(spec)
+    W = spec.pop("W")
+    case = small_case(**spec)
+    say(f"window {W} case {spec}: q_lens {case.q_lens.tolist()} kv_lens {case.kv_len.tolist()}")
+    O_ref, L_ref = oracle_attention(case, window=W)
+    dc = DeviceCase(case)
+    out, lse = run_attn(dc, window=W)
+    assert_close(out, O_ref, case.dtype, lse, L_ref, what=f"window {W}")
+    out2, _ = run_attn(dc, plan=False, want_lse=False, window=W)
+    assert torch.equal(out.view(torch.uint8) if out.dtype == torch.bfloat16 else out,
+                       out2.view(torch.uint8) if out2.dtype == torch.bfloat16 else out2)
+
+
+def test_window_wider_than_every_sequence_is_bit_identical():
+    case = small_case(59, G=4, d=128, D=16, P=16, batch=4, max_q=130, max_kv=500)
+    dc = DeviceCase(case)
+    out, lse = run_attn(dc)
+    outw, lsew = run_attn(dc, window=int(case.kv_len.max()) + case.max_q_len)
+    assert torch.equal(out.view(torch.uint8), outw.view(torch.uint8))
+    assert torch.equal(lse, lsew)
+
+
+def test_window_C2_decode_full(workloads):
+    case = workloads(2)
+    O_ref, L_ref = oracle_attention(case, window=1024)
+    out, lse = run_attn(DeviceCase(case), window=1024)
+    assert_close(out, O_ref, "bf16", lse, L_ref, what="C2 window 1024")
+
+
+def test_window_C5_long_context_sampled(workloads):
+    case = workloads(5)
+    order = np.argsort(case.kv_len)
+    seqs = list(order[:4]) + list(order[-4:]) + list(order[28:32])
+    rows = {int(s): np.array([0, 17, 38, 63]) for s in seqs}
+    O_ref, L_ref = oracle_attention(case, rows=rows, window=4096)
+    out, lse = run_attn(DeviceCase(case), window=4096)
+    assert_close(out, O_ref, "bf16", lse, L_ref, what="C5 window 4096 sampled")
+    assert torch.isfinite(out.float()).all()
 
 
 # Step-plan invariants. The plan is the library's internal work list (layout documented in
