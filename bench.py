@@ -93,9 +93,9 @@ def summarize_traffic(args):
            "hbm_bytes_per_call": out["fetch"]["bytes_per_call"] + out["write"]["bytes_per_call"],
            "fetch": out["fetch"], "write": out["write"],
            "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o f -- python3 bench.py "
-                        f"--config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --calib-copy",
+                        f"--config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --no-graph --calib-copy",
                         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o w -- python3 bench.py "
-                        f"--config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --calib-copy",
+                        f"--config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --no-graph --calib-copy",
                         f"python3 bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
                         f"--summarize-traffic <fetch csv> <write csv>"]}
     base = os.path.join(ROOT, "profiles", f"attn_traffic_C{args.config}")
