@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="skip the captured 32-layer model step")
     p.add_argument("--window", type=int, default=0,
                    help="sliding window in positions (mode A workloads; 0 = none)")
+    p.add_argument("--live-in-cache", action="store_true",
+                   help="live keys/values already in the pool at kv_len + i: attention reads one "
+                        "paged source and the commit moves only block ids")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, then WRITE_SIZE) of `bench.py --calib-copy` into "
@@ -235,7 +238,7 @@ def main():
     if args.window and case.q_blk is not None:
         print("--window applies to mode A workloads only", file=sys.stderr)
         sys.exit(2)
-    meta = bcp.StepMeta(**dc.meta_kwargs(), window=args.window)
+    meta = bcp.StepMeta(**dc.meta_kwargs(), window=args.window, live_in_cache=args.live_in_cache)
     plan = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda")
     nqt, nkt = bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
     tile_class = torch.empty((case.batch, nqt, nkt), dtype=torch.uint8, device="cuda")
@@ -247,14 +250,29 @@ def main():
     dst = dc.kv_len
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
+    k_live, v_live = (None, None) if args.live_in_cache else (dc.k_new, dc.v_new)
+    if args.live_in_cache:
+        # The producer's job, done once before timing: the live rows go to their slots
+        # (logical rows kv_len + i), where every step then reads them.
+        bcp.kv_commit_block(bcp.StepMeta(**dc.meta_kwargs()), dc.k_new, dc.v_new, dc.cu_q, dst, k_cache, v_cache,
+                            case.total_q)
+
+    def attn_call(m):
+        bcp.attn_block_causal_paged(m, dc.q, k_live, v_live, k_cache, v_cache, out, plan=plan, workspace=ws)
+
+    def commit_call(m):
+        # In place only the block ids move (mode B); in mode A nothing is launched.
+        bcp.kv_commit_block(m, k_live, v_live, dc.cu_q, dst, k_cache, v_cache, case.total_q,
+                            src_blk=dc.q_blk if args.live_in_cache else None,
+                            kv_blk_out=dc.kv_blk if args.live_in_cache else None, n_src=case.total_q)
+
     def step(evs=None):
         if evs: evs[0].record()
         bcp.build_tile_mask(meta, tile_class=tile_class, phys_page=phys if nct else None, plan=plan)
         if evs: evs[1].record()
-        bcp.attn_block_causal_paged(meta, dc.q, dc.k_new, dc.v_new, k_cache, v_cache, out, plan=plan,
-                                    workspace=ws)
+        attn_call(meta)
         if evs: evs[2].record()
-        bcp.kv_commit_block(meta, dc.k_new, dc.v_new, dc.cu_q, dst, k_cache, v_cache, case.total_q)
+        commit_call(meta)
         if evs: evs[3].record()
 
     for _ in range(args.warmup):
@@ -302,7 +320,7 @@ def main():
     for _ in range(n_warm):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         e[0].record()
-        bcp.attn_block_causal_paged(meta, dc.q, dc.k_new, dc.v_new, k_cache, v_cache, out, plan=plan, workspace=ws)
+        attn_call(meta)
         e[1].record()
         attn_warm.append(e)
     torch.cuda.synchronize()
@@ -313,15 +331,14 @@ def main():
     # call by call and replayed as one captured step graph, on the same side stream.
     graph_rec = None
     if not args.no_graph:
-        meta_u = bcp.StepMeta(**dc.meta_kwargs(), check=False, window=args.window)
+        meta_u = bcp.StepMeta(**dc.meta_kwargs(), check=False, window=args.window, live_in_cache=args.live_in_cache)
         gs = torch.cuda.Stream()
 
         def model_step():
             bcp.build_tile_mask(meta_u, tile_class=tile_class, phys_page=phys if nct else None, plan=plan)
             for _ in range(LAYERS):
-                bcp.attn_block_causal_paged(meta_u, dc.q, dc.k_new, dc.v_new, k_cache, v_cache, out, plan=plan,
-                                            workspace=ws)
-                bcp.kv_commit_block(meta_u, dc.k_new, dc.v_new, dc.cu_q, dst, k_cache, v_cache, case.total_q)
+                attn_call(meta_u)
+                commit_call(meta_u)
 
         n_rep = 5
         with torch.cuda.stream(gs):
@@ -365,7 +382,7 @@ def main():
     else:
         peak = MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else FP32_PEAK_TFLOPS
         achieved, unit = flops / (a_mean * 1e-6) / 1e12, "TFLOP/s"
-    traffic = None if args.window else traffic_from_profile(cfg)
+    traffic = None if args.window or args.live_in_cache else traffic_from_profile(cfg)
 
     rec = {
         "metric": METRIC,
@@ -385,7 +402,8 @@ def main():
                    "total_q": case.total_q, "kv_len_mean": float(case.kv_len.mean()),
                    "kv_len_max": int(case.kv_len.max()), "page_size": case.page_size,
                    "block_size": case.block_size, "mode": case.mode,
-                   **({"window": args.window} if args.window else {})},
+                   **({"window": args.window} if args.window else {}),
+                   **({"live_in_cache": True} if args.live_in_cache else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
                      "traffic": traffic,
@@ -402,7 +420,7 @@ def main():
         "mfma_frac": round(flops / (a_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "build_tile_mask_us": round(float(np.mean(cls_us)), 3),
         "kv_commit_us": round(float(np.mean(com_us)), 3),
-        "kv_commit_gbps": round(2 * live_kv / (float(np.mean(com_us)) * 1e-6) / 1e9, 1),
+        "kv_commit_gbps": None if args.live_in_cache else round(2 * live_kv / (float(np.mean(com_us)) * 1e-6) / 1e9, 1),
         "warm_step_us": round(warm_step_us, 3),
         "model_step_graph": graph_rec,
         "timed_wall_s_incl_flush": round(wall, 4),

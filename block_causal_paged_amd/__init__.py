@@ -21,6 +21,7 @@ BCP_BF16, BCP_F32 = 0, 1
 BCP_TILE_SKIP, BCP_TILE_PARTIAL, BCP_TILE_FULL = 0, 1, 2
 BCP_OK, BCP_E_ARG, BCP_E_UNSUPPORTED, BCP_E_RANGE, BCP_E_WORKSPACE, BCP_E_HIP = range(6)
 BCP_F_CHECK = 1
+BCP_F_LIVE_IN_CACHE = 2
 
 STATUS_NAMES = {0: "BCP_OK", 1: "BCP_E_ARG", 2: "BCP_E_UNSUPPORTED", 3: "BCP_E_RANGE",
                 4: "BCP_E_WORKSPACE", 5: "BCP_E_HIP"}
@@ -126,7 +127,8 @@ class StepMeta:
 
     def __init__(self, *, dtype, batch, num_q_heads, num_kv_heads, head_dim, block_size, cu_q,
                  kv_len, page_table, num_pages, page_size, total_q, max_q_len, max_kv_len,
-                 q_blk=None, kv_blk=None, tile_q=0, tile_k=0, check=False, window=0):
+                 q_blk=None, kv_blk=None, tile_q=0, tile_k=0, check=False, window=0,
+                 live_in_cache=False):
         self._refs = (cu_q, kv_len, page_table, q_blk, kv_blk)
         self.device_ref = cu_q
         self.c = bcp_meta(
@@ -137,7 +139,7 @@ class StepMeta:
             max_q_len=max_q_len, kv_len=_ptr(kv_len), page_table=_ptr(page_table),
             kv_blk=_ptr(kv_blk), num_pages=num_pages, page_size=page_size,
             max_pages_per_seq=int(page_table.shape[1]) if hasattr(page_table, "shape") else 1,
-            max_kv_len=max_kv_len, tile_q=tile_q, tile_k=tile_k, flags=BCP_F_CHECK if check else 0,
+            max_kv_len=max_kv_len, tile_q=tile_q, tile_k=tile_k, flags=(BCP_F_CHECK if check else 0) | (BCP_F_LIVE_IN_CACHE if live_in_cache else 0),
             window=int(window or 0),
         )
 
@@ -178,7 +180,8 @@ def attn_block_causal_paged(meta, q, k_new, v_new, k_cache, v_cache, out, plan=N
 
 def kv_commit_block(meta, k_src, v_src, cu_src, dst_start, k_cache, v_cache, total_commit,
                     src_row=None, src_blk=None, kv_blk_out=None, n_src=None, stream=None):
-    n_src = int(k_src.shape[0]) if n_src is None else n_src
+    if n_src is None:
+        n_src = int((k_src if k_src is not None else src_blk).shape[0])
     _check(lib().kv_commit_block(meta.ref, _ptr(k_src), _ptr(v_src), _ptr(cu_src), _ptr(src_row),
                                  _ptr(dst_start), _ptr(src_blk), int(total_commit), int(n_src),
                                  _ptr(k_cache), _ptr(v_cache), _ptr(kv_blk_out),

@@ -74,6 +74,7 @@ int check_meta(const bcp_meta* m, Geo* g) {
     return fail(BCP_E_ARG, "total_q %d exceeds batch * max_q_len", m->total_q);
   if ((int64_t)m->max_kv_len > (int64_t)m->max_pages_per_seq * m->page_size)
     return fail(BCP_E_ARG, "max_kv_len %d exceeds max_pages_per_seq * page_size", m->max_kv_len);
+  if (m->flags & ~(BCP_F_CHECK | BCP_F_LIVE_IN_CACHE)) return fail(BCP_E_ARG, "unknown flags 0x%x", m->flags);
   if ((int64_t)m->num_pages * m->page_size > INT32_MAX || (int64_t)m->batch * m->max_pages_per_seq > INT32_MAX)
     return fail(BCP_E_ARG, "pool or page table too large for 32-bit slot indices");
   if (m->window < 0) return fail(BCP_E_ARG, "window must be >= 0 (got %d)", m->window);
@@ -144,7 +145,11 @@ int validate_metadata(const bcp_meta* m, hipStream_t stream) {
       return fail(BCP_E_RANGE, "sequence %d: q_len %d outside [0, max_q_len %d]", s, ql, m->max_q_len);
     if (kvl[s] < 0 || kvl[s] > m->max_kv_len)
       return fail(BCP_E_RANGE, "sequence %d: kv_len %d outside [0, max_kv_len %d]", s, kvl[s], m->max_kv_len);
-    for (int64_t lp = 0; lp < ceil_div(kvl[s], m->page_size); ++lp) {
+    // Pages of the committed rows, and of the live rows when those are read from the pool.
+    const int64_t rows = kvl[s] + ((m->flags & BCP_F_LIVE_IN_CACHE) ? ql : 0);
+    if (rows > (int64_t)m->max_pages_per_seq * m->page_size)
+      return fail(BCP_E_RANGE, "sequence %d: kv_len + q_len = %lld exceeds the page table", s, (long long)rows);
+    for (int64_t lp = 0; lp < ceil_div(rows, m->page_size); ++lp) {
       const int p = pt[(size_t)s * m->max_pages_per_seq + lp];
       if (p < 0 || p >= m->num_pages)
         return fail(BCP_E_RANGE, "sequence %d: page_table[%lld] = %d outside [0, %d)", s, (long long)lp, p,
@@ -352,7 +357,9 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   int rc = check_meta(m, &g);
   if (rc) return rc;
   if ((rc = check_attention_shape(m, g))) return rc;
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
+  const bool in_place = (m->flags & BCP_F_LIVE_IN_CACHE) != 0;
+  if (in_place) k_new = v_new = nullptr;   // not read: the live rows come from the pool
+  if (!q || (!in_place && (!k_new || !v_new)) || !k_cache || !v_cache || !out)
     return fail(BCP_E_ARG, "q, k_new, v_new, k_cache, v_cache and out must be non-NULL");
   if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)) ||
@@ -414,6 +421,7 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   a.max_items = plan_layout(m->batch, g.nqt, g.nkt, m->num_kv_heads).max_items;
   a.page_shift = (m->page_size & (m->page_size - 1)) ? -1 : __builtin_ctz((unsigned)m->page_size);
   a.window = g.mode_b ? 0 : m->window;
+  a.live_in_cache = (m->flags & BCP_F_LIVE_IN_CACHE) != 0;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)m->head_dim);
   a.scale_log2 = sc * 1.4426950408889634f;
 
@@ -446,8 +454,12 @@ int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src, con
   const int64_t row_bytes = (int64_t)m->num_kv_heads * m->head_dim * esize;
   if (row_bytes % 16) return fail(BCP_E_UNSUPPORTED, "a cache row (%lld bytes) must be a multiple of 16 bytes",
                                   (long long)row_bytes);
-  if (!k_cache || !v_cache || !cu_src || !dst_start || (total_commit > 0 && (!k_src || !v_src)))
+  const bool in_place = (m->flags & BCP_F_LIVE_IN_CACHE) != 0;
+  if ((k_src == nullptr) != (v_src == nullptr)) return fail(BCP_E_ARG, "k_src and v_src must be both set or both NULL");
+  if (!k_cache || !v_cache || !cu_src || !dst_start || (total_commit > 0 && !k_src && !in_place))
     return fail(BCP_E_ARG, "k_src, v_src, cu_src, dst_start, k_cache and v_cache must be non-NULL");
+  if (!k_src && (src_blk == nullptr) != (kv_blk_out == nullptr))
+    return fail(BCP_E_ARG, "an in-place commit writes block ids only: src_blk and kv_blk_out go together");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || (k_src && !aligned(k_src, 16)) ||
       (v_src && !aligned(v_src, 16)))
     return fail(BCP_E_ARG, "K/V buffers must be 16-byte aligned");
@@ -482,7 +494,7 @@ int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src, con
     }
   }
   g_err.clear();
-  if (total_commit == 0) return BCP_OK;
+  if (total_commit == 0 || (!k_src && !kv_blk_out)) return BCP_OK;   // nothing to move
   CommitArgs a{};
   a.k_src = k_src;
   a.v_src = v_src;

@@ -74,6 +74,7 @@ constexpr int kRowsPerWave = kTileK / kWaves;   // key rows each wave stages per
 constexpr int kWin = 256;
 constexpr int kWinPerThread = kWin * kWaves / kThreads;   // window slots each thread stages
 constexpr int kEpRowBytes = 128;
+constexpr int kLivePages = 256;   // pages of an item's live rows staged in LDS when those sit in the pool
 template <int HD>
 struct AttnSmem {
   uint16_t k[kKStages][kTileK * HD];
@@ -81,6 +82,7 @@ struct AttnSmem {
   int kblk[kVStages][kTileK];      // block id of each key of a partial tile
   int win_e[kWin];                 // the item's plan entries, one window at a time
   int win_row[kWin][kWaves];       // first memory row of each wave's 8 rows, or -1
+  int live_pg[kLivePages];         // physical pages of the live rows' logical pages, when in the pool
   float ep[kWaves][32 * kEpRowBytes / 4];   // per-wave output staging
 };
 
@@ -154,6 +156,7 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertv
 
 struct Item {
   int s, g, q0, q_len, kvl;
+  int lp_live;   // logical page of row kv_len (the first live row when they sit in the pool)
 };
 
 template <int HD>
@@ -169,8 +172,10 @@ __device__ __forceinline__ int tile_valid(const AttnArgs& a, const Item& it, int
 }
 
 // Staging state of one key tile for one wave: the plan entry and the memory row of the
-// wave's first key row (rows of the kv cache for a cached tile, of the new keys for a live
-// tile), -1 when the wave's rows need the general path.
+// wave's first key row (rows of the kv cache for a cached tile, and for a live tile when
+// the live rows are read from the pool; else rows of the new keys), -1 when the wave's
+// rows need the general path, -(row) - 2 for a run of live rows in the pool that crosses
+// into the next page (row: its first row).
 struct Stage {
   int e;              // plan entry: (tile << 1) | is_partial; -1 when there is no tile
   int row0;
@@ -215,8 +220,9 @@ struct FastOffsets {
 // consecutive in memory (row0 >= 0), one wave-uniform base and fixed per-lane offsets
 // address them. Otherwise each lane resolves its own row through the page table, and an
 // absent key (past its region's length, or in a page outside the pool) copies the
-// sequence's first live row: absent keys only occur in partial tiles, where the mask gives
-// them weight exactly 0, and that row is finite, so it adds exactly nothing.
+// sequence's first live row (its first query row when the live rows are read from the
+// pool): absent keys only occur in partial tiles, where the mask gives them weight exactly
+// 0, and that row is finite, so it adds exactly nothing.
 template <int HD, int NI>
 __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st,
                                            AttnSmem<HD>& sm, int sk, int sv, const FastOffsets<HD>& fo) {
@@ -225,8 +231,9 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
   const int vt = st.e >> 1;
   const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const bool cached = vt < a.nct;
-  const uint16_t* kb = (const uint16_t*)(cached ? a.k_cache : a.k_new);
-  const uint16_t* vb = (const uint16_t*)(cached ? a.v_cache : a.v_new);
+  const bool paged = cached || a.live_in_cache;   // the tile's rows sit in the cache pool
+  const uint16_t* kb = (const uint16_t*)(paged ? a.k_cache : a.k_new);
+  const uint16_t* vb = (const uint16_t*)(paged ? a.v_cache : a.v_new);
   const int run0 = kRowsPerWave * wave;           // first tile row of this wave
   if (st.row0 >= 0) {
     const int64_t e0 = ((int64_t)st.row0 * a.Hkv + it.g) * HD;
@@ -236,28 +243,55 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       dma16s(kb + e0, fo.k[k], lds_addr(&sm.k[sk][base]));
       dma16s(vb + e0, fo.v[k], lds_addr(&sm.v[sv][base]));
     }
+  } else if (st.row0 <= -2) {
+    // Live rows in the pool whose run crosses a page boundary: the first `split` rows from
+    // the run's page, the rest from the next one (its id staged in LDS with the item).
+    const int row0 = -st.row0 - 2;
+    int lp0, slot0;
+    page_split(it.kvl + (vt - a.nct) * kTileK + run0, a.page_size, a.page_shift, &lp0, &slot0);
+    const int split = a.page_size - slot0;
+    const int64_t row1 = (int64_t)uni(sm.live_pg[lp0 + 1 - it.lp_live]) * a.page_size - split;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int rr = k * D::RPI + lane / D::CPR, r = run0 + rr, pch = lane % D::CPR;
+      const int64_t row = rr < split ? row0 + rr : row1 + rr;
+      const int base = (run0 + k * D::RPI) * HD;
+      dma16(kb + (row * a.Hkv + it.g) * HD + 8 * (pch ^ kswz<HD>(r)), lds_addr(&sm.k[sk][base]));
+      dma16(vb + (row * a.Hkv + it.g) * HD + 8 * (pch ^ vswz<HD>(r)), lds_addr(&sm.v[sv][base]));
+    }
   } else {
     const int nvalid = tile_valid(a, it, vt);
     const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
-    const int64_t sub = ((int64_t)it.q0 * a.Hkv + it.g) * HD;   // substitute row for absent keys
+    // Substitute row for absent keys: the item's first live key row, or, when the live
+    // rows are read from the pool, the item's first query row (equally finite).
+    const uint16_t* ksub = (const uint16_t*)a.k_new + ((int64_t)it.q0 * a.Hkv + it.g) * HD;
+    const uint16_t* vsub = (const uint16_t*)a.v_new + ((int64_t)it.q0 * a.Hkv + it.g) * HD;
+    if (a.live_in_cache)
+      ksub = vsub = (const uint16_t*)a.q + ((int64_t)it.q0 * a.Hq + (int64_t)it.g * a.G) * HD;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int r = run0 + k * D::RPI + lane / D::CPR;   // row inside the tile
       const int pch = lane % D::CPR;                     // physical chunk
       int64_t row = -1;
       if (r < nvalid) {
-        if (cached) {
+        if (paged) {
+          // Logical cache row: committed row j, or live row i at kv_len + i. A live row's
+          // page comes from LDS (staged with the item) when it is among the first
+          // kLivePages of the live region, so no load in the tile loop waits on memory.
+          const int j = cached ? vt * kTileK + r : it.kvl + (vt - a.nct) * kTileK + r;
           int lp, slot;
-          page_split(vt * kTileK + r, a.page_size, a.page_shift, &lp, &slot);
-          const int p = pt[min(lp, a.max_pages - 1)];
+          page_split(j, a.page_size, a.page_shift, &lp, &slot);
+          int p;
+          if (!cached && lp - it.lp_live < kLivePages) p = sm.live_pg[lp - it.lp_live];
+          else p = pt[min(lp, a.max_pages - 1)];
           if (p >= 0 && p < a.num_pages) row = (int64_t)p * a.page_size + slot;
         } else {
           row = it.q0 + (vt - a.nct) * kTileK + r;
         }
       }
       const bool ok = row >= 0;
-      const uint16_t* ksrc = ok ? kb + (row * a.Hkv + it.g) * HD : (const uint16_t*)a.k_new + sub;
-      const uint16_t* vsrc = ok ? vb + (row * a.Hkv + it.g) * HD : (const uint16_t*)a.v_new + sub;
+      const uint16_t* ksrc = ok ? kb + (row * a.Hkv + it.g) * HD : ksub;
+      const uint16_t* vsrc = ok ? vb + (row * a.Hkv + it.g) * HD : vsub;
       const int base = (run0 + k * D::RPI) * HD;
       dma16(ksrc + 8 * (pch ^ kswz<HD>(r)), lds_addr(&sm.k[sk][base]));
       dma16(vsrc + 8 * (pch ^ vswz<HD>(r)), lds_addr(&sm.v[sv][base]));
@@ -375,6 +409,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     it.q0 = ip[5];       // the unit's live rows and committed length, as the planner
     it.q_len = ip[6];    // clamped them
     it.kvl = ip[7];
+    it.lp_live = a.page_shift >= 0 ? it.kvl >> a.page_shift : it.kvl / a.page_size;
     const int i0 = r * a.tile_q;
     const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;
 
@@ -411,6 +446,25 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
               const int p = pt[lp];
               if (p >= 0 && p < a.num_pages) row0 = p * a.page_size + slot;
             }
+          } else if (a.live_in_cache) {
+            // Live rows in the pool at kv_len + i (kv_len need not be a multiple of
+            // anything): a run inside one page is one base; a run that crosses into the
+            // next page is stored as -(first row) - 2, its second page's id then coming
+            // from the staged live pages.
+            const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q, j0 = it.kvl + r0;
+            if (r0 + kRowsPerWave <= it.q_len && j0 + kRowsPerWave <= a.max_pages * a.page_size) {
+              int lp, slot;
+              page_split(j0, a.page_size, a.page_shift, &lp, &slot);
+              const int p = pt[lp];
+              if (p >= 0 && p < a.num_pages) {
+                if (slot + kRowsPerWave <= a.page_size) {
+                  row0 = p * a.page_size + slot;
+                } else if (kRowsPerWave - (a.page_size - slot) <= a.page_size && lp + 1 - it.lp_live < kLivePages) {
+                  const int p1 = pt[lp + 1];   // exists: the run's last row lies in page lp + 1
+                  if (p1 >= 0 && p1 < a.num_pages) row0 = -(p * a.page_size + slot) - 2;
+                }
+              }
+            }
           } else {
             const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q;
             if (r0 + kRowsPerWave <= it.q_len) row0 = it.q0 + r0;
@@ -420,6 +474,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       }
     };
     win_load_entries(ob, min(oe - ob, kWin));
+    // Live rows in the pool: the pages of their logical pages lp_live, lp_live+1, ...
+    int lpg = -1;
+    if (a.live_in_cache && tq < kLivePages && it.lp_live + tq < a.max_pages) lpg = pt[it.lp_live + tq];
     asm volatile("" ::: "memory");   // keep the plan-entry loads ahead of the query loads
 
     // Query fragments of this lane's column (B operand of S^T = K Q^T), held in registers
@@ -460,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
           sm.win_row[ti][q] = wr[k];
         }
       }
+      if (a.live_in_cache && wb == ob && tq < kLivePages) sm.live_pg[tq] = lpg;
       __syncthreads();
       // The query loads were issued before the page-table loads just waited for, so they
       // have landed: no wait for them falls inside the tile loop (where it would also wait

@@ -72,7 +72,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
           }
         } else {
           const int j = (vt - a.nct) * kTileK + kappa;
-          if (j < q_len) {
+          if (j < q_len && a.live_in_cache) {
+            // Live row j read from the pool at logical row kv_len + j.
+            const int p = translate_page(a.page_table, s, kvl + j, a.page_size, a.max_pages, a.num_pages);
+            if (p >= 0) {
+              const int64_t off = (((int64_t)p * a.page_size + ((kvl + j) % a.page_size)) * a.Hkv + g) * HD;
+              kp = (const float*)a.k_cache + off;
+              vp = (const float*)a.v_cache + off;
+            }
+          } else if (j < q_len) {
             const int64_t off = ((int64_t)(q0 + j) * a.Hkv + g) * HD;
             kp = (const float*)a.k_new + off;
             vp = (const float*)a.v_new + off;

@@ -119,6 +119,7 @@ struct AttnArgs {
       max_pages, block_size, mode_b, max_items;
   int page_shift;         // log2(page_size) when it is a power of two, else -1
   int window;             // sliding window in positions (mode A), 0 for none
+  int live_in_cache;      // live row i of a sequence is read from the pool at kv_len + i
   float scale_log2;       // softmax scale times log2(e)
 };
 

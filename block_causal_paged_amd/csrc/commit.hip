@@ -60,10 +60,31 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
   }
 }
 
+// Commit of rows whose keys and values were already written into their slots: only the
+// block ids move, one row per thread.
+__global__ __launch_bounds__(256) void commit_ids_kernel(CommitArgs a) {
+  for (int row = blockIdx.x * blockDim.x + threadIdx.x; row < a.total; row += gridDim.x * blockDim.x) {
+    const int src = a.src_row ? a.src_row[row] : row;
+    int lo = 0, hi = a.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_src[mid] <= row) lo = mid; else hi = mid;
+    }
+    const int r = row - a.cu_src[lo];
+    const int j = a.dst_start[lo] + r;
+    const int page = translate_page(a.page_table, lo, j, a.page_size, a.max_pages, a.num_pages);
+    if (src < 0 || src >= a.n_src || page < 0 || r < 0) continue;
+    a.kv_blk_out[(int64_t)page * a.page_size + (j % a.page_size)] = a.src_blk[src];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_commit(const CommitArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(commit_kernel, dim3(grid), dim3(256), 0, stream, a);
+  if (a.k_src)
+    hipLaunchKernelGGL(commit_kernel, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(commit_ids_kernel, dim3((a.total + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,14 @@ enum {
   BCP_E_HIP = 5           /* a HIP runtime call failed */
 };
 #define BCP_F_CHECK 1u    /* validate device metadata before launch (one device->host sync) */
+/* The live rows' keys and values already sit in the cache pool: live row i of sequence s
+ * at logical row kv_len[s] + i, written there by whatever produced them ("Inference: Fewer,
+ * smaller forwards", Advancement 11: the active block's entries live in the same arena as
+ * the committed ones, so committing them is a length change). Attention then reads one
+ * paged source of kv_len + q_len rows and ignores k_new/v_new (they may be NULL); the
+ * commit of such rows moves only their block ids (k_src = v_src = NULL). Each sequence
+ * needs pages mapped for its kv_len + q_len rows (checked mode verifies it). */
+#define BCP_F_LIVE_IN_CACHE 2u
 
 /*
  * Geometry of one step, shared by every call of the step (and every layer).
@@ -97,7 +105,7 @@ typedef struct bcp_meta {
   int32_t max_kv_len;          /* host bound on kv_len[s] */
   int32_t tile_q;              /* query positions per q-tile; 0 -> 256/(Hq/Hkv) */
   int32_t tile_k;              /* keys per k-tile; 0 -> 64 */
-  uint32_t flags;              /* BCP_F_CHECK */
+  uint32_t flags;              /* BCP_F_CHECK | BCP_F_LIVE_IN_CACHE */
   int32_t window;              /* sliding window W >= 1 in positions, or 0 for none (mode A only):
                                   key position pk stays visible to query position pq only if
                                   pq - pk < W, committed row j at position j and live row i at
@@ -147,7 +155,9 @@ size_t attn_block_causal_paged_workspace_size(const bcp_meta* m);
 /*
  * attn_block_causal_paged -- block-causal attention of the live rows over the paged cache
  * and the live rows themselves (definition at the top of this file).
- *   q, k_new, v_new, k_cache, v_cache: layouts above, dtype m->dtype.
+ *   q, k_new, v_new, k_cache, v_cache: layouts above, dtype m->dtype; with
+ *               BCP_F_LIVE_IN_CACHE the live keys and values are read from the caches at
+ *               logical rows kv_len[s] + i and k_new/v_new are ignored (may be NULL).
  *   plan        from build_tile_mask with the same meta, or NULL (then it is built in the
  *               workspace first, costing two extra kernel launches).
  *   scale       softmax scale; <= 0 selects 1/sqrt(head_dim).
@@ -183,6 +193,9 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
  *   cu_src [batch+1], src_row [total_commit] or NULL, dst_start [batch],
  *   src_blk [n_src] or NULL, kv_blk_out [num_pages*P] or NULL.
  *   total_commit = host copy of cu_src[batch]; n_src = rows in k_src/v_src.
+ * With BCP_F_LIVE_IN_CACHE, k_src = v_src = NULL commits rows that are already in their
+ * slots: only kv_blk_out[page*P+slot] = src_blk[row] is written (nothing at all when both
+ * are NULL, as in mode A, where committing such rows is the caller's kv_len update).
  * Two rows with the same destination slot race (checked mode rejects it with BCP_E_RANGE).
  * Uses m's dtype, batch, Hkv, head_dim, page_table, num_pages, page_size,
  * max_pages_per_seq and flags.

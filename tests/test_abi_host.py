@@ -77,6 +77,7 @@ def test_geometry_queries():
     (dict(tile_q=32), bcp.BCP_E_UNSUPPORTED),
     (dict(tile_k=32), bcp.BCP_E_UNSUPPORTED),
     (dict(window=-1), bcp.BCP_E_ARG),
+    (dict(flags=4), bcp.BCP_E_ARG),                       # unknown flag
     (dict(window=256, q_blk=FAKE, kv_blk=FAKE), bcp.BCP_E_UNSUPPORTED),   # window in mode B
 ])
 def test_attention_rejects_bad_meta(over, code):
@@ -93,6 +94,13 @@ def test_attention_rejects_bad_meta(over, code):
 ])
 def test_attention_rejects_bad_buffers(over, code):
     assert attn(meta(), **over) == code
+
+
+def test_live_rows_in_cache_need_no_separate_live_buffers():
+    # Without the flag NULL live buffers are refused; with it they are not read, so the call
+    # gets as far as the workspace check.
+    assert attn(meta(), k_new=None, v_new=None) == bcp.BCP_E_ARG
+    assert attn(meta(flags=bcp.BCP_F_LIVE_IN_CACHE), k_new=None, v_new=None, wsb=16) == bcp.BCP_E_WORKSPACE
 
 
 def test_tile_mask_rejects():
@@ -120,6 +128,11 @@ def test_commit_rejects():
     assert commit(meta(), total=-1) == bcp.BCP_E_ARG
     assert commit(meta(), v_src=FAKE + 4) == bcp.BCP_E_ARG
     assert commit(meta(head_dim=4, num_kv_heads=1)) == bcp.BCP_E_UNSUPPORTED   # 8-byte rows
+    assert commit(meta(), k_src=None) == bcp.BCP_E_ARG                         # one of the two
+    assert commit(meta(), k_src=None, v_src=None) == bcp.BCP_E_ARG             # in place needs the flag
+    inplace = meta(flags=bcp.BCP_F_LIVE_IN_CACHE)
+    assert commit(inplace, k_src=None, v_src=None, src_blk=FAKE) == bcp.BCP_E_ARG   # ids need kv_blk_out
+    assert commit(inplace, k_src=None, v_src=None) == bcp.BCP_OK              # mode A: nothing to move
     assert commit(meta(), total=0) == bcp.BCP_OK                              # nothing to do
 
 
