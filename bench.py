@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 FP32_PEAK_TFLOPS = 157.3
 # Which roof binds each workload (algorithmic FLOP/byte against the 314.6 FLOP/B ridge).
-BOUND = {1: "hbm", 2: "hbm", 3: "mfma", 4: "mfma", 5: "hbm"}
+BOUND = {1: "hbm", 2: "hbm", 3: "mfma", 4: "mfma", 5: "hbm", 6: "hbm"}
 KERNEL_SOURCES = ["attn_bf16.hip", "combine.hip"]
 LAYERS = 32   # layers of the model step that is also timed as a captured graph
 
@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2, help="workload number 1-5 (default 2)")
+    p.add_argument("--config", type=int, default=2, help="workload number 1-6 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain copy kernel of known size")

@@ -82,7 +82,11 @@ int check_meta(const bcp_meta* m, Geo* g) {
     return fail(BCP_E_UNSUPPORTED, "a sliding window is supported in mode A only");
   g->G = m->num_q_heads / m->num_kv_heads;
   g->mode_b = m->q_blk != nullptr;
-  g->tq = m->tile_q ? m->tile_q : std::max(1, kRowsPerWG / g->G);
+  // Short live blocks (at most kNarrowRows packed rows per sequence and kv head, bf16) get
+  // narrow q-tiles by default, which the narrow attention kernel handles.
+  const bool narrow = m->dtype == BCP_BF16 && kNarrowRows % g->G == 0 &&
+                      (int64_t)m->max_q_len * g->G <= kNarrowRows;
+  g->tq = m->tile_q ? m->tile_q : std::max(1, (narrow ? kNarrowRows : kRowsPerWG) / g->G);
   g->tk = m->tile_k ? m->tile_k : kTileK;
   if (g->tq < 1 || g->tq > 4096 || g->tk < 1 || g->tk > 4096)
     return fail(BCP_E_ARG, "tile sizes must lie in [1, 4096] (tile_q %d, tile_k %d)", g->tq, g->tk);
@@ -100,9 +104,10 @@ int check_attention_shape(const bcp_meta* m, const Geo& g) {
     return fail(BCP_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", m->head_dim);
   if (kRowsPerWG % g.G)
     return fail(BCP_E_UNSUPPORTED, "query heads per kv head (%d) must divide %d", g.G, kRowsPerWG);
-  if (g.tq != kRowsPerWG / g.G || g.tk != kTileK)
-    return fail(BCP_E_UNSUPPORTED, "attention needs tile_q = %d and tile_k = %d (got %d, %d)",
-                kRowsPerWG / g.G, kTileK, g.tq, g.tk);
+  const bool narrow_ok = m->dtype == BCP_BF16 && kNarrowRows % g.G == 0 && g.tq == kNarrowRows / g.G;
+  if ((g.tq != kRowsPerWG / g.G && !narrow_ok) || g.tk != kTileK)
+    return fail(BCP_E_UNSUPPORTED, "attention needs tile_q = %d (or %d for bf16) and tile_k = %d (got %d, %d)",
+                kRowsPerWG / g.G, kNarrowRows / g.G, kTileK, g.tq, g.tk);
   return BCP_OK;
 }
 
@@ -427,8 +432,10 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
 
   const int cus = device_cus();
   const int grid = kWGs;   // one workgroup per range of the plan
-  hipError_t e = m->dtype == BCP_BF16 ? launch_attn_bf16(a, m->head_dim, grid, stream)
-                                      : launch_attn_f32(a, m->head_dim, grid, stream);
+  const bool narrow = m->dtype == BCP_BF16 && g.tq * g.G == kNarrowRows;
+  hipError_t e = m->dtype != BCP_BF16 ? launch_attn_f32(a, m->head_dim, grid, stream)
+                 : narrow             ? launch_attn_bf16_narrow(a, m->head_dim, grid, stream)
+                                      : launch_attn_bf16(a, m->head_dim, grid, stream);
   if (e != hipSuccess) return hip_fail(e, "launch attention");
   if (part) {
     const int cgrid = (int)std::min<int64_t>((int64_t)kMaxPartialSlots * 16, (int64_t)cus * 8);

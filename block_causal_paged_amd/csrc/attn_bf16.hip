@@ -189,13 +189,13 @@ struct RawMeta {
   bool valid;       // wi < nt
 };
 
-template <int HD>
-__device__ __forceinline__ RawMeta meta_read(int wi, int nt, const AttnSmem<HD>& sm) {
-  const int wave = threadIdx.x >> 6, w = min(wi, kWin - 1);
+template <class Smem>
+__device__ __forceinline__ RawMeta meta_read(int wi, int nt, int q, const Smem& sm) {
+  const int w = min(wi, kWin - 1);
   RawMeta r;
   r.valid = wi < nt;
   r.e = sm.win_e[w];
-  r.row0 = sm.win_row[w][wave];
+  r.row0 = sm.win_row[w][q];
   return r;
 }
 
@@ -214,27 +214,27 @@ struct FastOffsets {
   unsigned k[DmaShape<HD>::NI], v[DmaShape<HD>::NI];
 };
 
-// Issue the direct loads of a resolved tile into key stage `sk` and value stage `sv`: NI K
-// and NI V wave instructions per wave, plus one block-id copy per wave for partial mode-B
-// tiles. Returns the number of loads issued. When the wave's 8 rows are present and
-// consecutive in memory (row0 >= 0), one wave-uniform base and fixed per-lane offsets
-// address them. Otherwise each lane resolves its own row through the page table, and an
+// Issue the direct loads of 8-row run q (rows 8q..8q+7) of a resolved tile into key stage
+// `sk` and value stage `sv`: NI K and NI V wave instructions, plus one block-id copy for
+// partial mode-B tiles. Returns the number of loads issued. When the run's 8 rows are
+// present and consecutive in memory (row0 >= 0), one wave-uniform base and fixed per-lane
+// offsets (fo, made for a run of the same parity) address them. Otherwise each lane resolves its own row through the page table, and an
 // absent key (past its region's length, or in a page outside the pool) copies the
 // sequence's first live row (its first query row when the live rows are read from the
 // pool): absent keys only occur in partial tiles, where the mask gives them weight exactly
 // 0, and that row is finite, so it adds exactly nothing.
-template <int HD, int NI>
-__device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st,
-                                           AttnSmem<HD>& sm, int sk, int sv, const FastOffsets<HD>& fo) {
+template <int HD, int NI, class Smem>
+__device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st, Smem& sm,
+                                           int sk, int sv, const FastOffsets<HD>& fo, int q) {
   using D = DmaShape<HD>;
   if (st.e < 0) return 0;
   const int vt = st.e >> 1;
-  const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const bool cached = vt < a.nct;
   const bool paged = cached || a.live_in_cache;   // the tile's rows sit in the cache pool
   const uint16_t* kb = (const uint16_t*)(paged ? a.k_cache : a.k_new);
   const uint16_t* vb = (const uint16_t*)(paged ? a.v_cache : a.v_new);
-  const int run0 = kRowsPerWave * wave;           // first tile row of this wave
+  const int run0 = kRowsPerWave * q;              // first tile row of the run
   if (st.row0 >= 0) {
     const int64_t e0 = ((int64_t)st.row0 * a.Hkv + it.g) * HD;
 #pragma unroll
@@ -331,6 +331,61 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
   return 2 * NI;
 }
 
+// First memory row of 8-row run q of each staged tile entry (see Stage): N slots per
+// thread, slot k being window slot tq + k*nthr (tile slot / kWaves, run slot % kWaves).
+// The page-table loads of all slots are issued together, unconditionally at a clamped
+// index, so that the staging costs one memory round trip rather than one per slot.
+template <int N>
+__device__ __forceinline__ void run_rows(const AttnArgs& a, const Item& it, const int32_t* pt, const int (&we)[N],
+                                         int tq, int nthr, int nt, int (&wr)[N]) {
+  const bool grp_pages = a.page_size % kRowsPerWave == 0;
+  const int cap = a.max_pages * a.page_size;
+  int lp[N], slot[N], kind[N];   // kind 1: cached run, 2: live run in the pool, else wr set
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int i = tq + k * nthr, q = i % kWaves, vt = we[k] >> 1;
+    kind[k] = 0;
+    lp[k] = slot[k] = 0;
+    wr[k] = -1;
+    if (i < nt * kWaves) {
+      if (vt < a.nct) {
+        const int j0 = vt * kTileK + kRowsPerWave * q;
+        if (grp_pages && j0 + kRowsPerWave <= it.kvl) {
+          kind[k] = 1;
+          page_split(j0, a.page_size, a.page_shift, &lp[k], &slot[k]);
+        }
+      } else if (a.live_in_cache) {
+        const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q, j0 = it.kvl + r0;
+        if (r0 + kRowsPerWave <= it.q_len && j0 + kRowsPerWave <= cap) {
+          kind[k] = 2;
+          page_split(j0, a.page_size, a.page_shift, &lp[k], &slot[k]);
+        }
+      } else {
+        const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q;
+        if (r0 + kRowsPerWave <= it.q_len) wr[k] = it.q0 + r0;
+      }
+    }
+  }
+  int p0[N], p1[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) p0[k] = pt[kind[k] ? lp[k] : 0];
+#pragma unroll
+  for (int k = 0; k < N; ++k) p1[k] = a.live_in_cache ? pt[kind[k] == 2 ? min(lp[k] + 1, a.max_pages - 1) : 0] : -1;
+  asm volatile("" ::: "memory");   // all loads issued here, not sunk into the uses below
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    if (!kind[k] || p0[k] < 0 || p0[k] >= a.num_pages) continue;
+    if (slot[k] + kRowsPerWave <= a.page_size) {
+      wr[k] = p0[k] * a.page_size + slot[k];
+    } else if (kind[k] == 2 && kRowsPerWave - (a.page_size - slot[k]) <= a.page_size &&
+               lp[k] + 1 - it.lp_live < kLivePages && p1[k] >= 0 && p1[k] < a.num_pages) {
+      // A live run crossing into the next page (its last row lies in page lp + 1, which
+      // therefore exists): stored as -(first row) - 2.
+      wr[k] = -(p0[k] * a.page_size + slot[k]) - 2;
+    }
+  }
+}
+
 // Wave schedule. The 8 waves form two groups, A = waves 0-3 and B = waves 4-7, one wave
 // of each per SIMD. Each tile t is handled in two phases per wave: a matrix phase
 // (S(t) = K(t) Q^T, then O += V(t-1) P(t-1)) and a vector phase (mask, online softmax
@@ -419,7 +474,6 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     // tid + k * kThreads (tile slot / 8, wave slot % 8); the loads come in two rounds (plan
     // entries, then page-table entries), issued apart from the LDS writes so that the first
     // window's rounds overlap the query loads.
-    const bool grp_pages = a.page_size % kRowsPerWave == 0;
     const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
     int we[kWinPerThread], wr[kWinPerThread];
     int tq = tid;
@@ -431,48 +485,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
       }
     };
-    auto win_load_rows = [&](int nt) {
-#pragma unroll
-      for (int k = 0; k < kWinPerThread; ++k) {
-        const int i = tq + k * kThreads, q = i % kWaves;
-        const int vt = we[k] >> 1;
-        int row0 = -1;
-        if (i < nt * kWaves) {
-          if (vt < a.nct) {
-            const int j0 = vt * kTileK + kRowsPerWave * q;
-            if (grp_pages && j0 + kRowsPerWave <= it.kvl) {
-              int lp, slot;
-              page_split(j0, a.page_size, a.page_shift, &lp, &slot);
-              const int p = pt[lp];
-              if (p >= 0 && p < a.num_pages) row0 = p * a.page_size + slot;
-            }
-          } else if (a.live_in_cache) {
-            // Live rows in the pool at kv_len + i (kv_len need not be a multiple of
-            // anything): a run inside one page is one base; a run that crosses into the
-            // next page is stored as -(first row) - 2, its second page's id then coming
-            // from the staged live pages.
-            const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q, j0 = it.kvl + r0;
-            if (r0 + kRowsPerWave <= it.q_len && j0 + kRowsPerWave <= a.max_pages * a.page_size) {
-              int lp, slot;
-              page_split(j0, a.page_size, a.page_shift, &lp, &slot);
-              const int p = pt[lp];
-              if (p >= 0 && p < a.num_pages) {
-                if (slot + kRowsPerWave <= a.page_size) {
-                  row0 = p * a.page_size + slot;
-                } else if (kRowsPerWave - (a.page_size - slot) <= a.page_size && lp + 1 - it.lp_live < kLivePages) {
-                  const int p1 = pt[lp + 1];   // exists: the run's last row lies in page lp + 1
-                  if (p1 >= 0 && p1 < a.num_pages) row0 = -(p * a.page_size + slot) - 2;
-                }
-              }
-            }
-          } else {
-            const int r0 = (vt - a.nct) * kTileK + kRowsPerWave * q;
-            if (r0 + kRowsPerWave <= it.q_len) row0 = it.q0 + r0;
-          }
-        }
-        wr[k] = row0;
-      }
-    };
+    auto win_load_rows = [&](int nt) { run_rows<kWinPerThread>(a, it, pt, we, tq, kThreads, nt, wr); };
     win_load_entries(ob, min(oe - ob, kWin));
     // Live rows in the pool: the pages of their logical pages lp_live, lp_live+1, ...
     int lpg = -1;
@@ -531,10 +544,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       // (group A: tile 0; group B: tiles 0 and 1), then tile 0 is published.
       int issued = 0;
       for (int x = 0; x < lead; ++x) {
-        const Stage st = meta_resolve(meta_read<HD>(x, nt, sm));
-        issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo);
+        const Stage st = meta_resolve(meta_read(x, nt, wave, sm));
+        issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo, uni(wave));
       }
-      RawMeta raw = meta_read<HD>(lead, nt, sm);           // next tile to issue
+      RawMeta raw = meta_read(lead, nt, wave, sm);         // next tile to issue
       int e_next = sm.win_e[0];                            // entry of the next tile to mask
       wait_vm(issued);
       __syncthreads();
@@ -600,8 +613,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       auto vector_phase = [&](int t) {
         {
           const int x = t + lead;
-          issued = stage_fetch<HD, NI>(a, it, meta_resolve(raw), sm, x % kKStages, x % kVStages, fo);
-          raw = meta_read<HD>(x + 1, nt, sm);
+          issued = stage_fetch<HD, NI>(a, it, meta_resolve(raw), sm, x % kKStages, x % kVStages, fo, uni(wave));
+          raw = meta_read(x + 1, nt, wave, sm);
         }
         const int e_t = uni(e_next);
         e_next = sm.win_e[min(t + 1, kWin - 1)];   // used next phase, only if t+1 < nt
@@ -775,6 +788,312 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Narrow items: live blocks of at most 64 packed rows per (sequence, kv head), such as a
+// short causal extend of up to 16 positions at four query heads per kv head.
+//
+// With so few live rows the wide kernel's 256-row work items would be mostly padding while
+// each key tile still costs the full matrix and softmax work. Here a workgroup of two waves
+// owns an item of 64 packed rows (32 per wave, each on its own SIMD). For each key tile each
+// wave stages four of its eight 8-row runs into a ring of kNStages stages, then computes
+// S = K Q^T, the mask and online softmax, and O += V P for its 32 rows. Loads run kNLead
+// tiles ahead; one barrier per tile publishes the tile (each wave has waited for its own
+// loads of it) and, since a wave passes it only after finishing the previous tile, also
+// frees the stage the next loads overwrite (kNLead + 2 <= kNStages).
+constexpr int kNWaves = 2, kNThreads = 64 * kNWaves;
+constexpr int kNStages = 4, kNLead = 2;
+constexpr int kNRuns = kWaves / kNWaves;            // 8-row runs each wave stages per tile
+constexpr int kNWinPerThread = kWin * kWaves / kNThreads;
+static_assert(kNLead == 2 && kNLead + 2 <= kNStages, "a stage is reused only after both waves left it");
+
+template <int HD>
+struct NarrowSmem {
+  uint16_t k[kNStages][kTileK * HD];
+  uint16_t v[kNStages][kTileK * HD];
+  int kblk[kNStages][kTileK];
+  int win_e[kWin];
+  int win_row[kWin][kWaves];       // per tile and 8-row run, as in the wide kernel
+  int live_pg[kLivePages];
+};
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI], by binary search over immediates.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_in(int n) {
+  if constexpr (LO == HI) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LO) : "memory");
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vm_in<LO, MID>(n);
+    else wait_vm_in<MID + 1, HI>(n);
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a) {
+  using D = DmaShape<HD>;
+  constexpr int NI = D::NI;
+  constexpr int NT = HD / 16, NDB = HD / 32;
+  static_assert(kNLead * kNRuns * (2 * NI + 1) + kNRuns * (2 * NI + 1) <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) NarrowSmem<HD> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hl = lane >> 5;
+  const int G = a.G;
+  const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
+  cint32* plan = as_const(a.plan);
+  cint32* rec = plan + L.rng + kRngWords * range_of_wg(blockIdx.x);
+  const int w_begin = rec[0], w_end = rec[1];
+  const uint16_t* qg = (const uint16_t*)a.q;
+  const float sl2 = a.scale_log2;
+  const int ta = (lane & 15) >> 2, tc = lane & 3;
+  const int vrow0 = 4 * hl + ta;
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * tc;
+  const int rho = wave * 32 + col;           // this lane's packed query row
+  int koff[NT], voff[NDB];
+  {
+    const int sw = kswz<HD>(col);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) koff[t] = col * HD + 8 * ((2 * t + hl) ^ sw);
+    const int vs = vswz<HD>(vrow0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int dcol = 32 * db + vcol0;
+      voff[db] = vrow0 * HD + ((dcol >> 3) ^ vs) * 8 + (dcol & 7);
+    }
+  }
+  // Fast-path offsets for runs of even and odd index (the K swizzle depends on the parity).
+  FastOffsets<HD> fo[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int rr = k * D::RPI + lane / D::CPR, r = kRowsPerWave * par + rr, pch = lane % D::CPR;
+      fo[par].k[k] = (unsigned)(((int64_t)rr * a.Hkv * HD + 8 * (pch ^ kswz<HD>(r))) * 2);
+      fo[par].v[k] = (unsigned)(((int64_t)rr * a.Hkv * HD + 8 * (pch ^ vswz<HD>(r))) * 2);
+    }
+  if (a.stats && blockIdx.x == 0 && tid == 0)
+    atomicAdd(&a.stats[2], (unsigned long long)a.Hkv * ((unsigned long long)L.units * a.nkt - plan[3]));
+
+  for (int item = w_begin; item < w_end; ++item) {
+    Item it;
+    cint32* ip = item == w_begin ? rec + 2 : plan + L.items + kItemWords * (int64_t)item;
+    const int u = ip[0], ob = ip[2], oe = ip[3], pslot = ip[4];
+    it.g = ip[1];
+    it.s = u / a.nqt;
+    const int r = u - it.s * a.nqt;
+    it.q0 = ip[5];
+    it.q_len = ip[6];
+    it.kvl = ip[7];
+    it.lp_live = a.page_shift >= 0 ? it.kvl >> a.page_shift : it.kvl / a.page_size;
+    const int i0 = r * a.tile_q;
+    const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;
+    const int32_t* pt = a.page_table + (int64_t)it.s * a.max_pages;
+
+    // Window staging, as in the wide kernel: plan entries, then the first memory row of
+    // every 8-row run of every tile (-1: general path; <= -2: a live run crossing a page).
+    auto win_stage = [&](int wb, int nt) {
+      int we[kNWinPerThread], wr[kNWinPerThread];
+#pragma unroll
+      for (int k = 0; k < kNWinPerThread; ++k) {
+        const int i = tid + k * kNThreads;
+        we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
+      }
+      run_rows<kNWinPerThread>(a, it, pt, we, tid, kNThreads, nt, wr);
+      __syncthreads();   // earlier readers of the window (previous window or item) are done
+#pragma unroll
+      for (int k = 0; k < kNWinPerThread; ++k) {
+        const int i = tid + k * kNThreads, ti = i / kWaves, q = i % kWaves;
+        if (i < nt * kWaves) {
+          if (q == 0) sm.win_e[ti] = we[k];
+          sm.win_row[ti][q] = wr[k];
+        }
+      }
+    };
+
+    // Query fragments and block id of this lane's row.
+    const int pos = i0 + rho / G, hh = rho - (rho / G) * G;
+    const bool qvalid = rho < a.tile_q * G && pos < it.q_len;
+    bf16x8 qf[NT];
+    {
+      const uint16_t* qp = qg + ((int64_t)(it.q0 + pos) * a.Hq + (int64_t)it.g * G + hh) * HD + 8 * hl;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bf16x8 z = {};
+        qf[t] = qvalid ? *(const bf16x8*)(qp + 16 * t) : z;
+      }
+    }
+    const int qblk = !qvalid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[it.q0 + pos] : pos / a.block_size);
+    int lpg[(kLivePages + kNThreads - 1) / kNThreads];
+#pragma unroll
+    for (int k = 0; k < (kLivePages + kNThreads - 1) / kNThreads; ++k) {
+      const int i = tid + k * kNThreads;
+      lpg[k] = a.live_in_cache && i < kLivePages && it.lp_live + i < a.max_pages ? pt[it.lp_live + i] : -1;
+    }
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+    int n_partial = 0;
+
+    for (int wb = ob; wb < oe; wb += kWin) {
+      const int nt = min(oe - wb, kWin);
+      win_stage(wb, nt);
+      if (wb == ob) {
+#pragma unroll
+        for (int k = 0; k < (kLivePages + kNThreads - 1) / kNThreads; ++k) {
+          const int i = tid + k * kNThreads;
+          if (i < kLivePages) sm.live_pg[i] = lpg[k];
+        }
+      }
+      __syncthreads();
+
+      // This wave's four runs of tile x into stage x % kNStages; returns the loads issued.
+      auto fetch = [&](int x) {
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < kNRuns; ++j) {
+          const int q = uni(wave) * kNRuns + j;
+          const Stage st = meta_resolve(meta_read(x, nt, q, sm));
+          n += stage_fetch<HD, NI>(a, it, st, sm, x % kNStages, x % kNStages, fo[j & 1], q);
+        }
+        return n;
+      };
+      // c2, c3: this wave's loads of tiles t+1 and t+2 (kNLead = 2).
+      fetch(0);
+      int c2 = fetch(1);
+      int e_next = sm.win_e[0];
+      for (int t = 0; t < nt; ++t) {
+        const int c3 = t + kNLead < nt ? fetch(t + kNLead) : 0;
+        wait_vm_in<0, 63>(c2 + c3);    // this wave's loads of tile t have landed
+        const int e_t = uni(e_next);
+        __syncthreads();               // and the other wave's; both left tile t-1
+        e_next = sm.win_e[min(t + 1, kWin - 1)];
+        c2 = c3;
+        const int st_ = t % kNStages;
+
+        // S^T = K Q^T for this wave's 32 rows (two 32-key blocks).
+        f32x16 sc[2];
+        {
+          const uint16_t* kt = sm.k[st_];
+#pragma unroll
+          for (int s = 0; s < NT; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const bf16x8 kf = *(const bf16x8*)&kt[koff[s] + 32 * kb * HD];
+              sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s == 0 ? f32x16{} : sc[kb], 0, 0, 0);
+            }
+        }
+        // Mask (partial tiles only) and online softmax, as in the wide kernel.
+        const bool partial = e_t & 1;
+        n_partial += partial;
+        if (partial) {
+          const int* kbl = sm.kblk[st_] + 4 * hl;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const i32x4 kbw = *(const i32x4*)&kbl[32 * kb + 8 * v4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (kbw[c] > qblk) sc[kb][4 * v4 + c] = -INFINITY;
+            }
+          if (a.window > 0) {
+            const int vt = e_t >> 1;
+            const int wbase = pos + (vt < a.nct ? it.kvl - vt * kTileK : -(vt - a.nct) * kTileK);
+            const int thr = wbase - a.window - 4 * hl;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v)
+                if (32 * kb + 8 * (v / 4) + v % 4 <= thr) sc[kb][v] = -INFINITY;
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
+        mx = half_max(mx);
+        const float mcand = mx * sl2;
+        const bool grow = mcand > m + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m - mcand) : 1.f;
+          m = grow ? mcand : m;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
+        const float muse = m == -INFINITY ? 0.f : m;
+        bf16x8 pf[2][2];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            f32x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hs + e], sl2, -muse));
+            pf[kb][hs] = to_bf16x8(x);
+            rs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+          }
+        l += rs;
+        // O^T += V^T P^T: step (kb, hs) covers keys 32kb+16hs .. +15 (see the wide kernel).
+        {
+          const uint16_t* vt = sm.v[st_];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const int rofs = (32 * kb + 16 * hs) * HD;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs]);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&vt[voff[db] + rofs + 8 * HD]);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hs], o[db], 0, 0, 0);
+              }
+        }
+      }
+    }   // window
+
+    // Epilogue: lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4 of row rho.
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+    if (qvalid) {
+      if (pslot < 0) {
+        const int64_t row = (int64_t)(it.q0 + pos) * a.Hq + (int64_t)it.g * G + hh;
+        uint16_t* op = (uint16_t*)a.out + row * HD + 4 * hl;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
+            *(bf16x4*)(op + 32 * db + 8 * v4) = __builtin_convertvector(x, bf16x4);
+          }
+        if (hl == 0 && a.lse) a.lse[row] = lse2 * kLn2;
+      } else {
+        float* pp = a.part_o + ((int64_t)pslot * kRowsPerWG + rho) * HD + 4 * hl;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
+            *(f32x4*)(pp + 32 * db + 8 * v4) = x;
+          }
+        if (hl == 0) a.part_lse[(int64_t)pslot * kRowsPerWG + rho] = lse2;
+      }
+    }
+    if (a.stats && tid == 0) {
+      const int n = oe - ob;
+      atomicAdd(&a.stats[0], (unsigned long long)(n - n_partial));
+      atomicAdd(&a.stats[1], (unsigned long long)n_partial);
+      atomicAdd(&a.stats[3], (unsigned long long)n * 2ull * kTileK * HD * 2ull);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
@@ -782,6 +1101,14 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream
     hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_narrow(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_bf16_narrow_kernel<128>, dim3(grid), dim3(kNThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_narrow_kernel<64>, dim3(grid), dim3(kNThreads), 0, stream, a);
   return hipGetLastError();
 }
 

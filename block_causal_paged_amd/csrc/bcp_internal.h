@@ -14,6 +14,7 @@ namespace bcp {
 // kTileK rows.
 constexpr int kTileK = 64;
 constexpr int kRowsPerWG = 256;
+constexpr int kNarrowRows = 64;   // packed rows of a narrow work item (short live blocks)
 
 // Split-KV planning. The work of a step is the sequence of (kv head, unit, key tile)
 // visits, ordered by kv head, then unit, then tile (a unit is one (sequence, q-tile); its
@@ -140,6 +141,7 @@ struct CommitArgs {
 hipError_t launch_classify(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_planner(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_attn_bf16_narrow(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, int head_dim, int is_bf16, int grid,
                           hipStream_t stream);

@@ -27,11 +27,13 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   // The loads of a work item form two rounds: its split record (with the work count), then
   // the sequence's live rows and every partial result at once; the partial addresses do not
   // depend on the live rows, and rows past the sequence's live rows are not stored.
-  for (int w = blockIdx.x; w < kWGs * NGRP; w += gridDim.x) {
-    const int grp = w % NGRP, e = w / NGRP;
+  // Row groups per split: all NGRP for 256-row q-tiles, fewer for narrow ones.
+  const int ngrp = min(NGRP, (a.tile_q * a.G + RPW - 1) / RPW);
+  for (int w = blockIdx.x; w < kWGs * ngrp; w += gridDim.x) {
+    const int grp = w % ngrp, e = w / ngrp;
     cint32* sp = plan + L.split + 4 * (int64_t)e;   // inside the kWGs split records
     const int u = sp[0], g = sp[1], ps0 = sp[2], n = sp[3];
-    if (w >= plan[1] * NGRP) break;
+    if (w >= plan[1] * ngrp) break;
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
     const int rho = grp * RPW + rr;
     float lc[MAXC];

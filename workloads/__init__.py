@@ -225,6 +225,7 @@ CONFIG_NAMES = {
     3: "prefill-commit: B4 32q/8kv d128 bf16, 8192-token prompt = 128 blocks of 64, P64 scattered",
     4: "multi-canvas: B16 32q/8kv d128 bf16, 1024 prompt + 3 canvases of 256, 30-100% live rows, P16",
     5: "long-context-decode: B64 32q/8kv d128 bf16 D64, kv lognormal clipped [1024,32768], P16",
+    6: "short-causal-extend: B64 32q/8kv d128 bf16 D1, 9 live rows (5 for a quarter), kv U{64..3072}, P16",
 }
 
 
@@ -256,6 +257,15 @@ def config(n: int, seed: Optional[int] = None) -> Case:
         return make_case(seed, name="C5", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
                          block_size=64, page_size=16, q_lens=[64] * 64, kv_lens=kv, qkv_std=inv,
                          rng=rng, desc=CONFIG_NAMES[5])
+    if n == 6:
+        # Extend steps at concurrency 64: 2N-1 = 9 causal query rows per sequence (N = 5),
+        # and N = 5 for a quarter of them (a proposal-only recovery step), over caches of
+        # prompt plus generated tokens.
+        ql = np.where(rng.random(64) < 0.25, 5, 9)
+        kv = rng.integers(64, 3073, size=64)
+        return make_case(seed, name="C6", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         block_size=1, page_size=16, q_lens=ql, kv_lens=kv, qkv_std=inv, rng=rng,
+                         desc=CONFIG_NAMES[6])
     raise ValueError(f"unknown config {n}")
 
 
