@@ -82,7 +82,7 @@ def summarize_traffic(args):
         factor = CALIB_BYTES / calib
         calls, cur = [], None
         for k, v in d:
-            if "attn_bf16_kernel" in k or "attn_f32_kernel" in k:
+            if "attn_bf16_kernel" in k or "attn_bf16_narrow_kernel" in k or "attn_f32_kernel" in k:
                 cur = [v]
                 calls.append(cur)
             elif "combine_kernel" in k and cur is not None:
@@ -373,6 +373,9 @@ def main():
         torch.cuda.synchronize()
 
     flops, cached_kv, live_kv, q_o = workload_stats(case, args.window)
+    G = case.num_q_heads // case.num_kv_heads
+    narrow = case.dtype == "bf16" and 64 % G == 0 and case.max_q_len * G <= 64
+    attn_kernel = "attn_f32_kernel" if case.dtype != "bf16" else ("attn_bf16_narrow_kernel" if narrow else "attn_bf16_kernel")
     algo_bytes = cached_kv + live_kv + q_o
     a_med = float(np.median(attn_us))
     a_mean = float(np.mean(attn_us))
@@ -407,7 +410,7 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     "kernel": "attn_block_causal_paged (attn_bf16_kernel + combine_kernel)",
+                     "kernel": f"attn_block_causal_paged ({attn_kernel} + combine_kernel)",
                      "algorithmic_bytes": algo_bytes, "useful_flops": flops,
                      "launch_us_mean": round(a_mean, 3)},
         "attention_us": {"median": round(a_med, 3), "mean": round(a_mean, 3),
