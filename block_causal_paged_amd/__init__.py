@@ -63,6 +63,8 @@ class bcp_meta(ctypes.Structure):
         ("tile_k", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("window", ctypes.c_int32),
+        ("q_pos", ctypes.c_void_p),
+        ("kv_pos", ctypes.c_void_p),
     ]
 
 
@@ -128,8 +130,8 @@ class StepMeta:
     def __init__(self, *, dtype, batch, num_q_heads, num_kv_heads, head_dim, block_size, cu_q,
                  kv_len, page_table, num_pages, page_size, total_q, max_q_len, max_kv_len,
                  q_blk=None, kv_blk=None, tile_q=0, tile_k=0, check=False, window=0,
-                 live_in_cache=False):
-        self._refs = (cu_q, kv_len, page_table, q_blk, kv_blk)
+                 live_in_cache=False, q_pos=None, kv_pos=None):
+        self._refs = (cu_q, kv_len, page_table, q_blk, kv_blk, q_pos, kv_pos)
         self.device_ref = cu_q
         self.c = bcp_meta(
             struct_size=ctypes.sizeof(bcp_meta),
@@ -140,7 +142,7 @@ class StepMeta:
             kv_blk=_ptr(kv_blk), num_pages=num_pages, page_size=page_size,
             max_pages_per_seq=int(page_table.shape[1]) if hasattr(page_table, "shape") else 1,
             max_kv_len=max_kv_len, tile_q=tile_q, tile_k=tile_k, flags=(BCP_F_CHECK if check else 0) | (BCP_F_LIVE_IN_CACHE if live_in_cache else 0),
-            window=int(window or 0),
+            window=int(window or 0), q_pos=_ptr(q_pos), kv_pos=_ptr(kv_pos),
         )
 
     @property

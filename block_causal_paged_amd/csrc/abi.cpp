@@ -78,8 +78,10 @@ int check_meta(const bcp_meta* m, Geo* g) {
   if ((int64_t)m->num_pages * m->page_size > INT32_MAX || (int64_t)m->batch * m->max_pages_per_seq > INT32_MAX)
     return fail(BCP_E_ARG, "pool or page table too large for 32-bit slot indices");
   if (m->window < 0) return fail(BCP_E_ARG, "window must be >= 0 (got %d)", m->window);
-  if (m->window > 0 && m->q_blk)
-    return fail(BCP_E_UNSUPPORTED, "a sliding window is supported in mode A only");
+  if (m->window > 0 && m->q_blk && (!m->q_pos || !m->kv_pos))
+    return fail(BCP_E_ARG, "a sliding window in mode B needs q_pos and kv_pos");
+  if (m->window > 0 && m->q_blk && (!aligned(m->q_pos, 4) || !aligned(m->kv_pos, 4)))
+    return fail(BCP_E_ARG, "q_pos and kv_pos must be 4-byte aligned");
   g->G = m->num_q_heads / m->num_kv_heads;
   g->mode_b = m->q_blk != nullptr;
   // Short live blocks (at most kNarrowRows packed rows per sequence and kv head, bf16) get
@@ -96,6 +98,9 @@ int check_meta(const bcp_meta* m, Geo* g) {
   g->nkt = g->nct + g->nlt;
   if ((int64_t)m->batch * g->nqt * g->nkt * 2 + 64 > INT32_MAX)
     return fail(BCP_E_ARG, "tile grid too large");
+  if (g->mode_b && m->window > 0 && g->nkt > kMaxBandKeyTiles)
+    return fail(BCP_E_UNSUPPORTED, "a window in mode B supports at most %d key tiles (got %d)", kMaxBandKeyTiles,
+                g->nkt);
   return BCP_OK;
 }
 
@@ -226,7 +231,11 @@ ClassifyArgs classify_args(const bcp_meta* m, const Geo& g) {
   a.phys_per_tile = std::max(1, g.tk / m->page_size);
   a.phys_tiles = g.nct;
   a.num_kv_heads = m->num_kv_heads;
-  a.window = g.mode_b ? 0 : m->window;
+  a.window = m->window;
+  if (g.mode_b && m->window > 0) {
+    a.q_pos = m->q_pos;
+    a.kv_pos = m->kv_pos;
+  }
   return a;
 }
 
@@ -425,7 +434,11 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   a.mode_b = g.mode_b;
   a.max_items = plan_layout(m->batch, g.nqt, g.nkt, m->num_kv_heads).max_items;
   a.page_shift = (m->page_size & (m->page_size - 1)) ? -1 : __builtin_ctz((unsigned)m->page_size);
-  a.window = g.mode_b ? 0 : m->window;
+  a.window = m->window;
+  if (g.mode_b && m->window > 0) {
+    a.q_pos = m->q_pos;
+    a.kv_pos = m->kv_pos;
+  }
   a.live_in_cache = (m->flags & BCP_F_LIVE_IN_CACHE) != 0;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)m->head_dim);
   a.scale_log2 = sc * 1.4426950408889634f;
@@ -461,12 +474,11 @@ int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src, con
   const int64_t row_bytes = (int64_t)m->num_kv_heads * m->head_dim * esize;
   if (row_bytes % 16) return fail(BCP_E_UNSUPPORTED, "a cache row (%lld bytes) must be a multiple of 16 bytes",
                                   (long long)row_bytes);
-  const bool in_place = (m->flags & BCP_F_LIVE_IN_CACHE) != 0;
   if ((k_src == nullptr) != (v_src == nullptr)) return fail(BCP_E_ARG, "k_src and v_src must be both set or both NULL");
-  if (!k_cache || !v_cache || !cu_src || !dst_start || (total_commit > 0 && !k_src && !in_place))
-    return fail(BCP_E_ARG, "k_src, v_src, cu_src, dst_start, k_cache and v_cache must be non-NULL");
+  if (!k_cache || !v_cache || !cu_src || !dst_start)
+    return fail(BCP_E_ARG, "cu_src, dst_start, k_cache and v_cache must be non-NULL");
   if (!k_src && (src_blk == nullptr) != (kv_blk_out == nullptr))
-    return fail(BCP_E_ARG, "an in-place commit writes block ids only: src_blk and kv_blk_out go together");
+    return fail(BCP_E_ARG, "a commit without k_src/v_src moves tags only: src_blk and kv_blk_out go together");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || (k_src && !aligned(k_src, 16)) ||
       (v_src && !aligned(v_src, 16)))
     return fail(BCP_E_ARG, "K/V buffers must be 16-byte aligned");

@@ -80,6 +80,7 @@ struct AttnSmem {
   uint16_t k[kKStages][kTileK * HD];
   uint16_t v[kVStages][kTileK * HD];
   int kblk[kVStages][kTileK];      // block id of each key of a partial tile
+  int kpos[kVStages][kTileK];      // and its position (mode B with a window)
   int win_e[kWin];                 // the item's plan entries, one window at a time
   int win_row[kWin][kWaves];       // first memory row of each wave's 8 rows, or -1
   int live_pg[kLivePages];         // physical pages of the live rows' logical pages, when in the pool
@@ -120,8 +121,8 @@ __device__ __forceinline__ void dma4(const void* g, unsigned lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(uni(lds)), "v"(g) : "memory");
 }
 // Wait until at most n of this wave's vector-memory loads are outstanding (they complete
-// in issue order, so everything issued before the last n has landed). n is 0, 2*NI or
-// 2*NI + 1 (a tile's loads), NI being 1 or 2.
+// in issue order, so everything issued before the last n has landed). n is 0 or a tile's
+// loads: 2*NI, plus one or two for partial mode-B tiles, NI being 1 or 2.
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
@@ -129,7 +130,8 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
     case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
     case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
   }
 }
 
@@ -223,7 +225,7 @@ struct FastOffsets {
 // sequence's first live row (its first query row when the live rows are read from the
 // pool): absent keys only occur in partial tiles, where the mask gives them weight exactly
 // 0, and that row is finite, so it adds exactly nothing.
-template <int HD, int NI, class Smem>
+template <int HD, int NI, bool BAND_B, class Smem>
 __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st, Smem& sm,
                                            int sk, int sv, const FastOffsets<HD>& fo, int q) {
   using D = DmaShape<HD>;
@@ -310,22 +312,54 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       // Keys that exist take their id from memory (a key in a page outside the pool gets
       // the sequence's first live row's id: its K and V were substituted by that row, so
       // it adds exactly nothing whatever its weight); absent keys get the id nobody sees.
-      const int32_t* src = a.q_blk + it.q0;
-      if (r < nvalid) {
-        if (!cached) {
-          src = a.q_blk + it.q0 + j;
-        } else if (st.row0 >= 0) {
-          src = a.kv_blk + st.row0 + (lane & 7);
-        } else {
-          int lp, slot;
-          page_split(j, a.page_size, a.page_shift, &lp, &slot);
-          const int p = a.page_table[(int64_t)it.s * a.max_pages + min(lp, a.max_pages - 1)];
-          if (p >= 0 && p < a.num_pages) src = a.kv_blk + (int64_t)p * a.page_size + slot;
+      if constexpr (!BAND_B) {
+        const int32_t* src = a.q_blk + it.q0;
+        if (r < nvalid) {
+          if (!cached) {
+            src = a.q_blk + it.q0 + j;
+          } else if (st.row0 >= 0) {
+            src = a.kv_blk + st.row0 + (lane & 7);
+          } else {
+            int lp, slot;
+            page_split(j, a.page_size, a.page_shift, &lp, &slot);
+            const int p = a.page_table[(int64_t)it.s * a.max_pages + min(lp, a.max_pages - 1)];
+            if (p >= 0 && p < a.num_pages) src = a.kv_blk + (int64_t)p * a.page_size + slot;
+          }
         }
+        if (lane < 8 && r >= nvalid) sm.kblk[sv][r] = kNoKeyBlk;
+        if (lane < 8 && r < nvalid) dma4(src, lds_addr(&sm.kblk[sv][run0]));
+        return 2 * NI + 1;
+      } else {
+        // With a window the keys' positions follow the same way, from the arrays beside
+        // the ids.
+        bool from_q = true;
+        int64_t off = it.q0;
+        if (r < nvalid) {
+          if (!cached) {
+            off = it.q0 + j;
+          } else if (st.row0 >= 0) {
+            from_q = false;
+            off = (int64_t)st.row0 + (lane & 7);
+          } else {
+            int lp, slot;
+            page_split(j, a.page_size, a.page_shift, &lp, &slot);
+            const int p = a.page_table[(int64_t)it.s * a.max_pages + min(lp, a.max_pages - 1)];
+            if (p >= 0 && p < a.num_pages) {
+              from_q = false;
+              off = (int64_t)p * a.page_size + slot;
+            }
+          }
+        }
+        if (lane < 8 && r >= nvalid) {
+          sm.kblk[sv][r] = kNoKeyBlk;
+          sm.kpos[sv][r] = 0;
+        }
+        if (lane < 8 && r < nvalid) {
+          dma4((from_q ? a.q_blk : a.kv_blk) + off, lds_addr(&sm.kblk[sv][run0]));
+          dma4((from_q ? a.q_pos : a.kv_pos) + off, lds_addr(&sm.kpos[sv][run0]));
+        }
+        return 2 * NI + 2;
       }
-      if (lane < 8 && r >= nvalid) sm.kblk[sv][r] = kNoKeyBlk;
-      if (lane < 8 && r < nvalid) dma4(src, lds_addr(&sm.kblk[sv][run0]));
-      return 2 * NI + 1;
     }
   }
   return 2 * NI;
@@ -401,7 +435,8 @@ __device__ __forceinline__ void run_rows(const AttnArgs& a, const Item& it, cons
 // reads it. K(x) is last read in H(2x+1), V(x) and the block ids of x in H(2x+3), all before
 // the loads of tile x+3 (keys) or x+4 (values) start in H(2x+2) or later: three key
 // stages and four value stages suffice.
-template <int HD>
+// BAND_B: mode B with a sliding window (keys' positions staged beside their block ids).
+template <int HD, bool BAND_B>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
@@ -506,6 +541,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     const int qblk = !qvalid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[it.q0 + pos] : pos / a.block_size);
+    int qpos = 0;
+    if constexpr (BAND_B) qpos = qvalid ? a.q_pos[it.q0 + pos] : 0;
     asm volatile("" ::: "memory");   // the page-table loads follow the query loads
     win_load_rows(min(oe - ob, kWin));
 
@@ -538,6 +575,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(qf[t]));
       asm volatile("" ::"v"(qblk));
+      if constexpr (BAND_B) asm volatile("" ::"v"(qpos));
       auto entry = [&](int t) { return t < nt ? sm.win_e[t] : -1; };
 
       // Prologue: tiles 0 .. lead-1 issued; this wave waits for all of them but the last
@@ -545,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       int issued = 0;
       for (int x = 0; x < lead; ++x) {
         const Stage st = meta_resolve(meta_read(x, nt, wave, sm));
-        issued = stage_fetch<HD, NI>(a, it, st, sm, x % kKStages, x % kVStages, fo, uni(wave));
+        issued = stage_fetch<HD, NI, BAND_B>(a, it, st, sm, x % kKStages, x % kVStages, fo, uni(wave));
       }
       RawMeta raw = meta_read(lead, nt, wave, sm);         // next tile to issue
       int e_next = sm.win_e[0];                            // entry of the next tile to mask
@@ -613,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       auto vector_phase = [&](int t) {
         {
           const int x = t + lead;
-          issued = stage_fetch<HD, NI>(a, it, meta_resolve(raw), sm, x % kKStages, x % kVStages, fo, uni(wave));
+          issued = stage_fetch<HD, NI, BAND_B>(a, it, meta_resolve(raw), sm, x % kKStages, x % kVStages, fo, uni(wave));
           raw = meta_read(x + 1, nt, wave, sm);
         }
         const int e_t = uni(e_next);
@@ -632,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
               for (int c = 0; c < 4; ++c)
                 if (kbw[c] > qblk) sc[kb][4 * v4 + c] = -INFINITY;
             }
-          if (a.window > 0) {
+          if (a.window > 0 && !a.mode_b) {
             // Sliding window (mode A): the key in column cc of the tile lies wbase - cc
             // positions before this lane's query (committed row j at position j, live row
             // i at kv_len + i); it drops out once that distance reaches the window.
@@ -644,6 +682,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
               for (int v = 0; v < 16; ++v)
                 if (32 * kb + 8 * (v / 4) + v % 4 <= thr) sc[kb][v] = -INFINITY;
+          } else if constexpr (BAND_B) {
+            // Sliding window (mode B): the keys' positions were staged beside their ids.
+            const int* kpl = sm.kpos[t % kVStages] + 4 * hl;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4) {
+                const i32x4 kpw = *(const i32x4*)&kpl[32 * kb + 8 * v4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  if ((int64_t)qpos - kpw[c] >= a.window) sc[kb][4 * v4 + c] = -INFINITY;
+              }
           }
         }
         // Online softmax in the log2 domain, with a lazy reference max: m only moves when
@@ -811,6 +861,7 @@ struct NarrowSmem {
   uint16_t k[kNStages][kTileK * HD];
   uint16_t v[kNStages][kTileK * HD];
   int kblk[kNStages][kTileK];
+  int kpos[kNStages][kTileK];
   int win_e[kWin];
   int win_row[kWin][kWaves];       // per tile and 8-row run, as in the wide kernel
   int live_pg[kLivePages];
@@ -828,12 +879,14 @@ __device__ __forceinline__ void wait_vm_in(int n) {
   }
 }
 
-template <int HD>
+template <int HD, bool BAND_B>
 __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a) {
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16, NDB = HD / 32;
-  static_assert(kNLead * kNRuns * (2 * NI + 1) + kNRuns * (2 * NI + 1) <= 63, "vmcnt range");
+  // Loads in flight per wave stay within the 6-bit counter: three tiles of at most
+  // kNRuns * (2*NI + 1) each, or, when positions are staged too (2*NI + 2 per run), two.
+  static_assert((kNLead + 1) * kNRuns * (2 * NI + 1) <= 63 && kNLead * kNRuns * (2 * NI + 2) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) NarrowSmem<HD> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -923,6 +976,8 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
       }
     }
     const int qblk = !qvalid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[it.q0 + pos] : pos / a.block_size);
+    int qpos = 0;
+    if constexpr (BAND_B) qpos = qvalid ? a.q_pos[it.q0 + pos] : 0;
     int lpg[(kLivePages + kNThreads - 1) / kNThreads];
 #pragma unroll
     for (int k = 0; k < (kLivePages + kNThreads - 1) / kNThreads; ++k) {
@@ -955,7 +1010,7 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
         for (int j = 0; j < kNRuns; ++j) {
           const int q = uni(wave) * kNRuns + j;
           const Stage st = meta_resolve(meta_read(x, nt, q, sm));
-          n += stage_fetch<HD, NI>(a, it, st, sm, x % kNStages, x % kNStages, fo[j & 1], q);
+          n += stage_fetch<HD, NI, BAND_B>(a, it, st, sm, x % kNStages, x % kNStages, fo[j & 1], q);
         }
         return n;
       };
@@ -964,8 +1019,14 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
       int c2 = fetch(1);
       int e_next = sm.win_e[0];
       for (int t = 0; t < nt; ++t) {
-        const int c3 = t + kNLead < nt ? fetch(t + kNLead) : 0;
-        wait_vm_in<0, 63>(c2 + c3);    // this wave's loads of tile t have landed
+        int c3;
+        if constexpr (BAND_B) {   // positions staged: land tile t before issuing more
+          wait_vm_in<0, 63>(c2);
+          c3 = t + kNLead < nt ? fetch(t + kNLead) : 0;
+        } else {
+          c3 = t + kNLead < nt ? fetch(t + kNLead) : 0;
+          wait_vm_in<0, 63>(c2 + c3);    // this wave's loads of tile t have landed
+        }
         const int e_t = uni(e_next);
         __syncthreads();               // and the other wave's; both left tile t-1
         e_next = sm.win_e[min(t + 1, kWin - 1)];
@@ -998,7 +1059,7 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
               for (int c = 0; c < 4; ++c)
                 if (kbw[c] > qblk) sc[kb][4 * v4 + c] = -INFINITY;
             }
-          if (a.window > 0) {
+          if (a.window > 0 && !a.mode_b) {
             const int vt = e_t >> 1;
             const int wbase = pos + (vt < a.nct ? it.kvl - vt * kTileK : -(vt - a.nct) * kTileK);
             const int thr = wbase - a.window - 4 * hl;
@@ -1007,6 +1068,18 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
 #pragma unroll
               for (int v = 0; v < 16; ++v)
                 if (32 * kb + 8 * (v / 4) + v % 4 <= thr) sc[kb][v] = -INFINITY;
+          } else if constexpr (BAND_B) {
+            // Sliding window (mode B): the keys' positions were staged beside their ids.
+            const int* kpl = sm.kpos[st_] + 4 * hl;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4) {
+                const i32x4 kpw = *(const i32x4*)&kpl[32 * kb + 8 * v4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  if ((int64_t)qpos - kpw[c] >= a.window) sc[kb][4 * v4 + c] = -INFINITY;
+              }
           }
         }
         float mx = -INFINITY;
@@ -1097,18 +1170,28 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+  const bool band_b = a.mode_b && a.window > 0;
+  if (head_dim == 128 && !band_b)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (!band_b)
+    hipLaunchKernelGGL((attn_bf16_kernel<64, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16_narrow(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_bf16_narrow_kernel<128>, dim3(grid), dim3(kNThreads), 0, stream, a);
+  const bool band_b = a.mode_b && a.window > 0;
+  if (head_dim == 128 && !band_b)
+    hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false>), dim3(grid), dim3(kNThreads), 0, stream, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, true>), dim3(grid), dim3(kNThreads), 0, stream, a);
+  else if (!band_b)
+    hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false>), dim3(grid), dim3(kNThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_bf16_narrow_kernel<64>, dim3(grid), dim3(kNThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, true>), dim3(grid), dim3(kNThreads), 0, stream, a);
   return hipGetLastError();
 }
 

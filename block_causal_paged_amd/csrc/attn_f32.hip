@@ -18,6 +18,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float ks[kTileK][HD];
   __shared__ __attribute__((aligned(16))) float vs[kTileK][HD];
   __shared__ int kblk[kTileK];
+  __shared__ int kpos[kTileK];   // positions of a partial tile's keys (mode B with a window)
   constexpr int V4 = HD / 4;
   const int tid = threadIdx.x;
   const int G = a.G;
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       ov[d] = 0.f;
     }
     const int qblk = !valid ? kNoKeyBlk - 1 : (a.mode_b ? a.q_blk[q0 + pos] : pos / a.block_size);
+    const int qpos = valid && a.q_pos ? a.q_pos[q0 + pos] : 0;
     float m = -INFINITY, l = 0.f;
     int n_partial = 0;
 
@@ -91,23 +93,27 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         *(f32x4*)&vs[kappa][4 * c] = vp ? *(const f32x4*)(vp + 4 * c) : z;
       }
       if (partial && tid < kTileK) {
-        int b;
+        int b, kp = 0;
         if (vt < a.nct) {
           const int j = vt * kTileK + tid;
           const int p = j < kvl ? translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages) : -1;
           b = p < 0 ? kNoKeyBlk : (a.mode_b ? a.kv_blk[(int64_t)p * a.page_size + (j % a.page_size)] : kNegInfBlk);
+          if (p >= 0 && a.kv_pos) kp = a.kv_pos[(int64_t)p * a.page_size + (j % a.page_size)];
         } else {
           const int j = (vt - a.nct) * kTileK + tid;
           b = j >= q_len ? kNoKeyBlk : (a.mode_b ? a.q_blk[q0 + j] : j / a.block_size);
+          if (j < q_len && a.q_pos) kp = a.q_pos[q0 + j];
         }
         kblk[tid] = b;
+        kpos[tid] = kp;
       }
       __syncthreads();
 
       // Sliding window (mode A): key k of the tile lies wbase - k positions before this
       // row's query (committed row j at position j, live row i at kv_len + i).
       const int wbase = pos + (vt < a.nct ? kvl - vt * kTileK : -(vt - a.nct) * kTileK);
-      const bool band = partial && a.window > 0;
+      const bool band = partial && a.window > 0 && !a.mode_b;
+      const bool band_b = partial && a.window > 0 && a.mode_b;
       float sc[kTileK];
       float mx = -INFINITY;
 #pragma unroll
@@ -123,6 +129,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         }
         if (partial && kblk[k] > qblk) acc = -INFINITY;
         if (band && wbase - k >= a.window) acc = -INFINITY;
+        if (band_b && (int64_t)qpos - kpos[k] >= a.window) acc = -INFINITY;
         sc[k] = acc;
         mx = fmaxf(mx, acc);
       }

@@ -15,6 +15,7 @@ namespace bcp {
 constexpr int kTileK = 64;
 constexpr int kRowsPerWG = 256;
 constexpr int kNarrowRows = 64;   // packed rows of a narrow work item (short live blocks)
+constexpr int kMaxBandKeyTiles = 2048;   // key tiles per q-tile row with a window in mode B
 
 // Split-KV planning. The work of a step is the sequence of (kv head, unit, key tile)
 // visits, ordered by kv head, then unit, then tile (a unit is one (sequence, q-tile); its
@@ -88,7 +89,9 @@ struct ClassifyArgs {
   int batch, total_q, tile_q, tile_k, nqt, nct, nkt, block_size, page_size, num_pages,
       max_pages, max_q_len, mode_b, phys_per_tile, phys_tiles, num_kv_heads;
   int grid_q;             // q-tile workgroups per sequence: max(nqt, 1)
-  int window;             // sliding window in positions (mode A), 0 for none
+  int window;             // sliding window in positions, 0 for none
+  const int32_t* q_pos;   // mode B with a window: position of each live row
+  const int32_t* kv_pos;  //   and of each cache slot
 };
 
 struct PlanArgs {
@@ -119,8 +122,10 @@ struct AttnArgs {
   int batch, total_q, max_q_len, Hq, Hkv, G, tile_q, nqt, nkt, nct, page_size, num_pages,
       max_pages, block_size, mode_b, max_items;
   int page_shift;         // log2(page_size) when it is a power of two, else -1
-  int window;             // sliding window in positions (mode A), 0 for none
+  int window;             // sliding window in positions, 0 for none
   int live_in_cache;      // live row i of a sequence is read from the pool at kv_len + i
+  const int32_t* q_pos;   // mode B with a window: position of each live row
+  const int32_t* kv_pos;  //   and of each cache slot
   float scale_log2;       // softmax scale times log2(e)
 };
 

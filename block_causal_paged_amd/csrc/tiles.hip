@@ -81,7 +81,8 @@ __device__ int block_max_nonneg(int v, int* lds) {
   return m;
 }
 
-constexpr int kClsLdsTiles = 2048;   // key tiles whose mode-B block-id ranges fit in LDS
+constexpr int kClsLdsTiles = kMaxBandKeyTiles;   // key tiles whose mode-B block-id ranges fit in LDS
+constexpr int kClsLdsRows = 512;     // q-tile rows staged in LDS for the exact mode-B window classes
 
 // Classifies q-tile r of sequence s (one workgroup of 256 threads; every thread calls it).
 __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
@@ -151,6 +152,60 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
     __syncthreads();
   }
 
+  // Mode B with a sliding window: a key is visible to a row iff its block id is not later
+  // and it lies fewer than W positions before the row. Block-id and position ranges alone
+  // cannot tell whether some pair meets both, so each key tile is classified from its
+  // pairs: one wave per tile, one lane per key, every row of the q-tile in turn (rows
+  // staged in LDS). The host rejects grids with more than kClsLdsTiles key tiles here.
+  __shared__ unsigned char s_cls[kClsLdsTiles];
+  __shared__ int s_qb[kClsLdsRows], s_qp[kClsLdsRows];
+  const bool band_b = a.mode_b && a.window > 0 && has_tiles && nrows > 0;
+  if (band_b) {
+    for (int i = tid; i < min(nrows, kClsLdsRows); i += blockDim.x) {
+      s_qb[i] = a.q_blk[q0 + i0 + i];
+      s_qp[i] = a.q_pos[q0 + i0 + i];
+    }
+    __syncthreads();
+    for (int t = wave; t < a.nkt; t += blockDim.x / 64) {
+      const bool cached = t < a.nct;
+      const int lo = (cached ? t : t - a.nct) * a.tile_k;
+      const int nvalid = clampi((cached ? kvl : q_len) - lo, 0, a.tile_k);
+      int any = 0, all = 1;   // over this lane's keys and every row
+      for (int jj = lane; jj < a.tile_k; jj += 64) {
+        const int j = lo + jj;
+        int kb = kNoKeyBlk, kp = 0;
+        if (jj < nvalid) {
+          if (cached) {
+            const int p = translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages);
+            if (p >= 0) {
+              const int64_t slot = (int64_t)p * a.page_size + (j % a.page_size);
+              kb = a.kv_blk[slot];
+              kp = a.kv_pos[slot];
+            }
+          } else {
+            kb = a.q_blk[q0 + j];
+            kp = a.q_pos[q0 + j];
+          }
+        }
+        int key_any = 0, key_all = kb != kNoKeyBlk;
+        for (int i = 0; i < nrows; ++i) {
+          const int qb = i < kClsLdsRows ? s_qb[i] : a.q_blk[q0 + i0 + i];
+          const int qp = i < kClsLdsRows ? s_qp[i] : a.q_pos[q0 + i0 + i];
+          const bool vis = kb <= qb && (int64_t)qp - kp < a.window;
+          key_any |= vis;
+          key_all &= vis;
+        }
+        any |= key_any;
+        all &= key_all;
+      }
+      any = __builtin_amdgcn_ballot_w64(any) != 0;
+      all = __builtin_amdgcn_ballot_w64(!all) == 0 && nvalid == a.tile_k;
+      if (lane == 0 && t < kClsLdsTiles)
+        s_cls[t] = (unsigned char)(!any ? BCP_TILE_SKIP : all ? BCP_TILE_FULL : BCP_TILE_PARTIAL);
+    }
+    __syncthreads();
+  }
+
   const int64_t list_base = (int64_t)u * a.nkt;
   PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.num_kv_heads);
   int running = 0;
@@ -199,7 +254,8 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
       if (nvalid == 0 || kmin > qmax) cls = BCP_TILE_SKIP;
       else if (kmax <= qmin && nvalid == a.tile_k) cls = BCP_TILE_FULL;
       else cls = BCP_TILE_PARTIAL;
-      if (a.window > 0 && cls != BCP_TILE_SKIP) {
+      if (band_b) cls = s_cls[t];
+      if (!a.mode_b && a.window > 0 && cls != BCP_TILE_SKIP) {
         // Sliding window (mode A): query row i sits at position kvl + i, committed key j at
         // j and live key j at kvl + j; a key is in the band while the query is fewer than
         // W positions past it. Rows i0..i1-1 against keys lo..hi of the tile:

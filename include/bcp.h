@@ -15,8 +15,9 @@
  *     mode B: to committed row j iff kv_blk[slot(j)] <= q_blk[i], and to live row j iff
  *             q_blk[j] <= q_blk[i] (block ids per row, as in multi-canvas decoding where
  *             canvas c sees the prompt, earlier canvases and itself);
- *   with a sliding window W (mode A), additionally only to keys at most W-1 positions
- *   before the query (committed row j at position j, live row i at kv_len + i).
+ *   with a sliding window W, additionally only to keys at most W-1 positions before the
+ *   query (mode A: committed row j at position j, live row i at kv_len + i; mode B: the
+ *   positions q_pos and kv_pos give, as arena entries carry their absolute position).
  *   out = softmax(scale * q k^T restricted to visible keys) v, per query head, with
  *   grouped-query attention: query head h reads kv head h / (Hq / Hkv).
  *   When a block is finished its rows are committed: copied bit for bit into the page
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define BCP_ABI_VERSION 2
+#define BCP_ABI_VERSION 3
 
 enum { BCP_BF16 = 0, BCP_F32 = 1 };
 enum { BCP_TILE_SKIP = 0, BCP_TILE_PARTIAL = 1, BCP_TILE_FULL = 2 };
@@ -106,11 +107,16 @@ typedef struct bcp_meta {
   int32_t tile_q;              /* query positions per q-tile; 0 -> 256/(Hq/Hkv) */
   int32_t tile_k;              /* keys per k-tile; 0 -> 64 */
   uint32_t flags;              /* BCP_F_CHECK | BCP_F_LIVE_IN_CACHE */
-  int32_t window;              /* sliding window W >= 1 in positions, or 0 for none (mode A only):
-                                  key position pk stays visible to query position pq only if
-                                  pq - pk < W, committed row j at position j and live row i at
-                                  kv_len + i ("Inference: Fewer, smaller forwards", Advancement
-                                  11); tiles entirely outside the window are SKIP */
+  int32_t window;              /* sliding window W >= 1 in positions, or 0 for none: key
+                                  position pk stays visible to query position pq only if
+                                  pq - pk < W ("Inference: Fewer, smaller forwards", Advancement
+                                  11); in mode A committed row j is at position j and live row i
+                                  at kv_len + i, in mode B q_pos/kv_pos give them; tiles entirely
+                                  outside the window are SKIP */
+  const int32_t* q_pos;        /* [total_q] position of each live row; mode B with a window only */
+  const int32_t* kv_pos;       /* [num_pages*page_size] position of each cache slot, beside
+                                  kv_blk; mode B with a window only (committed with an id-only
+                                  kv_commit_block, src_blk = q_pos, kv_blk_out = kv_pos) */
 } bcp_meta;
 
 /* Number of query tiles / key tiles of the step's tile grid (after the tile defaults).
@@ -193,9 +199,10 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
  *   cu_src [batch+1], src_row [total_commit] or NULL, dst_start [batch],
  *   src_blk [n_src] or NULL, kv_blk_out [num_pages*P] or NULL.
  *   total_commit = host copy of cu_src[batch]; n_src = rows in k_src/v_src.
- * With BCP_F_LIVE_IN_CACHE, k_src = v_src = NULL commits rows that are already in their
- * slots: only kv_blk_out[page*P+slot] = src_blk[row] is written (nothing at all when both
- * are NULL, as in mode A, where committing such rows is the caller's kv_len update).
+ * With k_src = v_src = NULL only the int32 tags move: kv_blk_out[page*P+slot] = src_blk[row]
+ * (nothing at all when both are NULL). That commits rows whose keys and values already sit
+ * in their slots (BCP_F_LIVE_IN_CACHE; in mode A committing them is then the caller's
+ * kv_len update), and it commits position tags (src_blk = q_pos, kv_blk_out = kv_pos).
  * Two rows with the same destination slot race (checked mode rejects it with BCP_E_RANGE).
  * Uses m's dtype, batch, Hkv, head_dim, page_table, num_pages, page_size,
  * max_pages_per_seq and flags.

@@ -9,18 +9,19 @@ import torch
 import oracle
 
 
-def oracle_attention(case, rows=None, scale=None, window=None):
+def oracle_attention(case, rows=None, scale=None, window=None, q_pos=None, kv_pos=None):
     return oracle.attention(case.q, case.k_new, case.v_new, case.k_cache, case.v_cache, case.cu_q,
                             case.kv_len, case.page_table, case.page_size, case.num_pages,
                             block_size=case.block_size, scale=scale, q_blk=case.q_blk,
-                            kv_blk=case.kv_blk, rows=rows, window=window)
+                            kv_blk=case.kv_blk, rows=rows, window=window, q_pos=q_pos, kv_pos=kv_pos)
 
 
-def oracle_tiles(case, tile_q, tile_k, window=None):
+def oracle_tiles(case, tile_q, tile_k, window=None, q_pos=None, kv_pos=None):
     return oracle.tile_classes(case.cu_q, case.kv_len, tile_q, tile_k, case.max_q_len,
                                case.max_kv_len, block_size=case.block_size, q_blk=case.q_blk,
                                kv_blk=case.kv_blk, page_table=case.page_table,
-                               page_size=case.page_size, num_pages=case.num_pages, window=window)
+                               page_size=case.page_size, num_pages=case.num_pages, window=window,
+                               q_pos=q_pos, kv_pos=kv_pos)
 
 
 def sdpa64(q, k, v, causal=False, mask=None, scale=None):

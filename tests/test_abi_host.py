@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_function():
     assert set(decl) == set(bcp.EXPORTED), decl
     for name in decl:
         assert hasattr(L, name), name
-    assert L.bcp_abi_version() == 2
+    assert L.bcp_abi_version() == 3
 
 
 def meta(**over):
@@ -78,7 +78,7 @@ def test_geometry_queries():
     (dict(tile_k=32), bcp.BCP_E_UNSUPPORTED),
     (dict(window=-1), bcp.BCP_E_ARG),
     (dict(flags=4), bcp.BCP_E_ARG),                       # unknown flag
-    (dict(window=256, q_blk=FAKE, kv_blk=FAKE), bcp.BCP_E_UNSUPPORTED),   # window in mode B
+    (dict(window=256, q_blk=FAKE, kv_blk=FAKE), bcp.BCP_E_ARG),     # window in mode B needs positions
 ])
 def test_attention_rejects_bad_meta(over, code):
     assert attn(meta(**over)) == code
@@ -129,7 +129,7 @@ def test_commit_rejects():
     assert commit(meta(), v_src=FAKE + 4) == bcp.BCP_E_ARG
     assert commit(meta(head_dim=4, num_kv_heads=1)) == bcp.BCP_E_UNSUPPORTED   # 8-byte rows
     assert commit(meta(), k_src=None) == bcp.BCP_E_ARG                         # one of the two
-    assert commit(meta(), k_src=None, v_src=None) == bcp.BCP_E_ARG             # in place needs the flag
+    assert commit(meta(), k_src=None, v_src=None) == bcp.BCP_OK                # no K/V and no tags: nothing
     inplace = meta(flags=bcp.BCP_F_LIVE_IN_CACHE)
     assert commit(inplace, k_src=None, v_src=None, src_blk=FAKE) == bcp.BCP_E_ARG   # ids need kv_blk_out
     assert commit(inplace, k_src=None, v_src=None) == bcp.BCP_OK              # mode A: nothing to move
