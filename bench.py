@@ -124,9 +124,11 @@ def summarize_traffic(args):
 def workload_stats(case, window=0):
     """Useful FLOPs (4*d per visible (row, key, query head)) and algorithmic bytes.
 
-    With a sliding window W (mode A), live row i sits at position kv_len + i and sees the
-    committed rows j > kv_len + i - W and the live rows j > i - W of its block or earlier
-    ones; only the committed rows that some live row sees (the last W - 1) count as bytes.
+    With a sliding window W, live row i sees only keys fewer than W positions before it: in
+    mode A committed row j sits at position j and live row i at kv_len + i, so live row i sees
+    the committed rows j > kv_len + i - W and the live rows j > i - W of its block or earlier
+    ones; in mode B the workload's positions decide. Only the committed rows that some live
+    row sees count as bytes.
     """
     import numpy as np
     d, Hq, Hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
@@ -135,7 +137,6 @@ def workload_stats(case, window=0):
     cached_rows = 0
     for s in range(case.batch):
         ql, kl = int(case.q_lens[s]), int(case.kv_len[s])
-        cached_rows += kl if not window else min(kl, window - 1)
         if case.q_blk is None:
             i = np.arange(ql)
             live = np.minimum(ql, (i // case.block_size + 1) * case.block_size)
@@ -143,14 +144,29 @@ def workload_stats(case, window=0):
                 cached = np.clip(window - 1 - i, 0, kl)
                 live = live - np.maximum(0, i - window + 1)
                 visible += int((cached + live).sum())
-                continue
-            visible += int((kl + live).sum())
+                cached_rows += min(kl, window - 1)
+            else:
+                visible += int((kl + live).sum())
+                cached_rows += kl
+        elif window:
+            # Mode B with a window: pairs with a block id not later and a position fewer than
+            # W before the row's (positions of the multi-canvas layout).
+            lo = int(case.cu_q[s])
+            qb, qp = case.q_blk[lo:lo + ql].astype(np.int64), case.q_pos[lo:lo + ql].astype(np.int64)
+            j = np.arange(kl)
+            slots = case.page_table[s, j // case.page_size].astype(np.int64) * case.page_size + j % case.page_size
+            kb = np.concatenate([case.kv_blk[slots].astype(np.int64), qb])
+            kp = np.concatenate([case.kv_pos[slots].astype(np.int64), qp])
+            vis = (kb[None, :] <= qb[:, None]) & (qp[:, None] - kp[None, :] < window)
+            visible += int(vis.sum())
+            cached_rows += int(vis[:, :kl].any(axis=0).sum())
         else:
             qb = np.sort(case.q_blk_seqs[s])
             kb = np.sort(case.kv_blk_seqs[s])
             rows = case.q_blk_seqs[s]
             visible += int(np.searchsorted(kb, rows, side="right").sum()
                            + np.searchsorted(qb, rows, side="right").sum())
+            cached_rows += kl
     flops = 4.0 * d * Hq * visible
     cached_kv = float(cached_rows) * Hkv * d * esize * 2
     live_kv = float(case.total_q) * Hkv * d * esize * 2
@@ -199,7 +215,9 @@ def cpu_baseline(case, budget_s, window=0):
         oracle.attention_rows(case.q, case.k_new, case.v_new, case.k_cache, case.v_cache, case.cu_q,
                               case.kv_len, case.page_table, case.page_size, case.num_pages, s,
                               block_size=case.block_size, q_blk=case.q_blk, kv_blk=case.kv_blk,
-                              window=window or None)
+                              window=window or None,
+                              q_pos=case.q_pos if window and case.q_blk is not None else None,
+                              kv_pos=case.kv_pos if window and case.q_blk is not None else None)
         rows_done += int(case.q_lens[s])
         seqs += 1
         if time.perf_counter() - t0 > budget_s:
@@ -235,8 +253,8 @@ def main():
     case = config(cfg)
     dc = DeviceCase(case)
     torch.cuda.synchronize()
-    if args.window and case.q_blk is not None:
-        print("--window applies to mode A workloads only", file=sys.stderr)
+    if args.window and case.q_blk is not None and case.q_pos is None:
+        print("--window in mode B needs a workload with positions (C4)", file=sys.stderr)
         sys.exit(2)
     meta = bcp.StepMeta(**dc.meta_kwargs(), window=args.window, live_in_cache=args.live_in_cache)
     plan = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda")

@@ -83,6 +83,7 @@ __device__ int block_max_nonneg(int v, int* lds) {
 
 constexpr int kClsLdsTiles = kMaxBandKeyTiles;   // key tiles whose mode-B block-id ranges fit in LDS
 constexpr int kClsLdsRows = 512;     // q-tile rows staged in LDS for the exact mode-B window classes
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 // Classifies q-tile r of sequence s (one workgroup of 256 threads; every thread calls it).
 __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
@@ -124,7 +125,8 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
   // Mode B: block-id range of every key tile, computed cooperatively (one wave per tile,
   // one lane per key) into LDS when the grid fits; each thread then classifies its tiles.
   __shared__ int s_kmin[kClsLdsTiles], s_kmax[kClsLdsTiles];
-  const bool coop = a.mode_b && has_tiles && nrows > 0 && a.nkt <= kClsLdsTiles;
+  // (With a window the classes come from the pass below instead.)
+  const bool coop = a.mode_b && a.window == 0 && has_tiles && nrows > 0 && a.nkt <= kClsLdsTiles;
   if (coop) {
     for (int t = wave; t < a.nkt; t += blockDim.x / 64) {
       int mn = INT32_MAX, mx = INT32_MIN;
@@ -153,55 +155,123 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
   }
 
   // Mode B with a sliding window: a key is visible to a row iff its block id is not later
-  // and it lies fewer than W positions before the row. Block-id and position ranges alone
-  // cannot tell whether some pair meets both, so each key tile is classified from its
-  // pairs: one wave per tile, one lane per key, every row of the q-tile in turn (rows
-  // staged in LDS). The host rejects grids with more than kClsLdsTiles key tiles here.
+  // and it lies fewer than W positions before the row. One wave per key tile, one lane per
+  // key: the tile is SKIP when its block ids or its positions are out of every row's reach,
+  // FULL when both are within every row's reach (these range tests are exact), and
+  // otherwise it is classified from its pairs, every row of the q-tile (staged in LDS) in
+  // turn. The host rejects grids with more than kClsLdsTiles key tiles here.
   __shared__ unsigned char s_cls[kClsLdsTiles];
-  __shared__ int s_qb[kClsLdsRows], s_qp[kClsLdsRows];
+  __shared__ __attribute__((aligned(16))) int s_q2[kClsLdsRows][2];   // (block id, position) per row
   const bool band_b = a.mode_b && a.window > 0 && has_tiles && nrows > 0;
   if (band_b) {
-    for (int i = tid; i < min(nrows, kClsLdsRows); i += blockDim.x) {
-      s_qb[i] = a.q_blk[q0 + i0 + i];
-      s_qp[i] = a.q_pos[q0 + i0 + i];
+    int pmn = INT32_MAX, pmx = INT32_MIN;
+    for (int i = tid; i < nrows; i += blockDim.x) {
+      const int b = a.q_blk[q0 + i0 + i], p = a.q_pos[q0 + i0 + i];
+      pmn = min(pmn, p);
+      pmx = max(pmx, p);
+      if (i < kClsLdsRows) {
+        s_q2[i][0] = b;
+        s_q2[i][1] = p;
+      }
     }
+    pmn = wave_min(pmn);
+    pmx = wave_max(pmx);
     __syncthreads();
+    if (lane == 0) { red[0][wave] = pmn; red[1][wave] = pmx; }
+    __syncthreads();
+    const int64_t qpmin = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+    const int64_t qpmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
     for (int t = wave; t < a.nkt; t += blockDim.x / 64) {
       const bool cached = t < a.nct;
       const int lo = (cached ? t : t - a.nct) * a.tile_k;
       const int nvalid = clampi((cached ? kvl : q_len) - lo, 0, a.tile_k);
-      int any = 0, all = 1;   // over this lane's keys and every row
-      for (int jj = lane; jj < a.tile_k; jj += 64) {
+      int kb = kNoKeyBlk, kp = 0, cls = BCP_TILE_SKIP;
+      int bmn = INT32_MAX, bmx = INT32_MIN, kpmn = INT32_MAX, kpmx = INT32_MIN;
+      for (int jj = lane; jj < a.tile_k; jj += 64) {   // one key per lane when tile_k <= 64
         const int j = lo + jj;
-        int kb = kNoKeyBlk, kp = 0;
+        int b = kNoKeyBlk, p = 0;
         if (jj < nvalid) {
           if (cached) {
-            const int p = translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages);
-            if (p >= 0) {
-              const int64_t slot = (int64_t)p * a.page_size + (j % a.page_size);
-              kb = a.kv_blk[slot];
-              kp = a.kv_pos[slot];
+            const int pg = translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages);
+            if (pg >= 0) {
+              const int64_t slot = (int64_t)pg * a.page_size + (j % a.page_size);
+              b = a.kv_blk[slot];
+              p = a.kv_pos[slot];
             }
           } else {
-            kb = a.q_blk[q0 + j];
-            kp = a.q_pos[q0 + j];
+            b = a.q_blk[q0 + j];
+            p = a.q_pos[q0 + j];
+          }
+          bmn = min(bmn, b);
+          bmx = max(bmx, b);
+          if (b != kNoKeyBlk) {
+            kpmn = min(kpmn, p);
+            kpmx = max(kpmx, p);
           }
         }
-        int key_any = 0, key_all = kb != kNoKeyBlk;
-        for (int i = 0; i < nrows; ++i) {
-          const int qb = i < kClsLdsRows ? s_qb[i] : a.q_blk[q0 + i0 + i];
-          const int qp = i < kClsLdsRows ? s_qp[i] : a.q_pos[q0 + i0 + i];
-          const bool vis = kb <= qb && (int64_t)qp - kp < a.window;
-          key_any |= vis;
-          key_all &= vis;
-        }
-        any |= key_any;
-        all &= key_all;
+        if (jj < 64) { kb = b; kp = p; }
       }
-      any = __builtin_amdgcn_ballot_w64(any) != 0;
-      all = __builtin_amdgcn_ballot_w64(!all) == 0 && nvalid == a.tile_k;
-      if (lane == 0 && t < kClsLdsTiles)
-        s_cls[t] = (unsigned char)(!any ? BCP_TILE_SKIP : all ? BCP_TILE_FULL : BCP_TILE_PARTIAL);
+      bmn = wave_min(bmn);
+      bmx = wave_max(bmx);
+      kpmn = wave_min(kpmn);
+      kpmx = wave_max(kpmx);
+      if (nvalid == 0 || bmn > qmax || kpmn == INT32_MAX || qpmin - kpmx >= a.window) {
+        cls = BCP_TILE_SKIP;
+      } else if (bmx <= qmin && nvalid == a.tile_k && qpmax - kpmn < a.window) {
+        cls = BCP_TILE_FULL;
+      } else if (a.tile_k <= 64 && nrows <= kClsLdsRows) {
+        // Pairs: any / all over this lane's key and every row (two rows per LDS read).
+        int any = 0, all = lane < nvalid && kb != kNoKeyBlk;
+        const int64_t reach = (int64_t)kp + a.window;   // visible iff qb >= kb and qp < reach
+        int i = 0;
+        for (; i + 1 < nrows; i += 2) {
+          const i32x4 w = *(const i32x4*)&s_q2[i][0];
+          const bool v0 = w[0] >= kb && w[1] < reach, v1 = w[2] >= kb && w[3] < reach;
+          any |= v0 | v1;
+          all &= v0 & v1;
+        }
+        if (i < nrows) {
+          const bool v0 = s_q2[i][0] >= kb && s_q2[i][1] < reach;
+          any |= v0;
+          all &= v0;
+        }
+        any &= lane < nvalid;
+        const bool tany = __builtin_amdgcn_ballot_w64(any) != 0;
+        const bool tall = nvalid == a.tile_k && __builtin_amdgcn_ballot_w64(lane < nvalid && !all) == 0;
+        cls = !tany ? BCP_TILE_SKIP : tall ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
+      } else {
+        // Tiles wider than a wave or q-tiles longer than the staging: pairs from memory.
+        int any = 0, all = 1;
+        for (int jj = lane; jj < a.tile_k; jj += 64) {
+          const int j = lo + jj;
+          int b = kNoKeyBlk, p = 0;
+          if (jj < nvalid) {
+            if (cached) {
+              const int pg = translate_page(a.page_table, s, j, a.page_size, a.max_pages, a.num_pages);
+              if (pg >= 0) {
+                const int64_t slot = (int64_t)pg * a.page_size + (j % a.page_size);
+                b = a.kv_blk[slot];
+                p = a.kv_pos[slot];
+              }
+            } else {
+              b = a.q_blk[q0 + j];
+              p = a.q_pos[q0 + j];
+            }
+          }
+          int key_any = 0, key_all = jj < nvalid && b != kNoKeyBlk;
+          for (int r2 = 0; r2 < nrows; ++r2) {
+            const bool v = b <= a.q_blk[q0 + i0 + r2] && (int64_t)a.q_pos[q0 + i0 + r2] - p < a.window;
+            key_any |= v;
+            key_all &= v;
+          }
+          any |= key_any & (jj < nvalid);
+          if (jj < nvalid) all &= key_all;
+        }
+        const bool tany = __builtin_amdgcn_ballot_w64(any) != 0;
+        const bool tall = nvalid == a.tile_k && __builtin_amdgcn_ballot_w64(!all) == 0;
+        cls = !tany ? BCP_TILE_SKIP : tall ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
+      }
+      if (lane == 0 && t < kClsLdsTiles) s_cls[t] = (unsigned char)cls;
     }
     __syncthreads();
   }
@@ -212,7 +282,9 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
   for (int base = 0; has_tiles && base < a.nkt; base += blockDim.x) {
     const int t = base + tid;
     int cls = BCP_TILE_SKIP;
-    if (t < a.nkt && nrows > 0) {
+    if (t < a.nkt && band_b) {
+      cls = s_cls[t];
+    } else if (t < a.nkt && nrows > 0) {
       int nvalid, kmin, kmax;
       if (t < a.nct) {
         const int lo = t * a.tile_k;
@@ -254,7 +326,6 @@ __device__ void classify_unit(const ClassifyArgs& a, int s, int r) {
       if (nvalid == 0 || kmin > qmax) cls = BCP_TILE_SKIP;
       else if (kmax <= qmin && nvalid == a.tile_k) cls = BCP_TILE_FULL;
       else cls = BCP_TILE_PARTIAL;
-      if (band_b) cls = s_cls[t];
       if (!a.mode_b && a.window > 0 && cls != BCP_TILE_SKIP) {
         // Sliding window (mode A): query row i sits at position kvl + i, committed key j at
         // j and live key j at kvl + j; a key is in the band while the query is fewer than

@@ -42,3 +42,21 @@ def test_flop_count_matches_dense_mask_mode_B():
                      page_size=8, q_lens=q_lens, kv_lens=kv_lens, q_blk_seqs=qb, kv_blk_seqs=kb, rng=rng)
     flops, _, _, _ = bench.workload_stats(case)
     assert flops == 4.0 * 64 * 2 * _dense_visible(case)
+
+
+def test_flop_count_matches_dense_mask_mode_B_window():
+    from workloads import multi_canvas_structure, with_positions
+    rng = np.random.default_rng(9)
+    ql, kl, qb, kb, lp, cp = multi_canvas_structure(rng, 3, 30, 12, 3)
+    case = with_positions(make_case(9, dtype="bf16", num_q_heads=2, num_kv_heads=1, head_dim=64, block_size=1,
+                                    page_size=8, q_lens=ql, kv_lens=kl, q_blk_seqs=qb, kv_blk_seqs=kb, rng=rng),
+                          lp, cp)
+    for W in (1, 7, 25):
+        flops, _, _, _ = bench.workload_stats(case, W)
+        n = 0
+        for s in range(case.batch):
+            lo, hi = int(case.cu_q[s]), int(case.cu_q[s + 1])
+            n += int(oracle.dense_mask(hi - lo, int(case.kv_len[s]), q_blk=case.q_blk_seqs[s],
+                                       kv_blk=case.kv_blk_seqs[s], window=W, q_pos=case.q_pos[lo:hi],
+                                       kv_pos=np.asarray(cp[s])).sum())
+        assert flops == 4.0 * 64 * 2 * n

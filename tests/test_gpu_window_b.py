@@ -15,7 +15,7 @@ import block_causal_paged_amd as bcp
 import oracle
 from tests.oracle_helpers import oracle_attention, oracle_tiles
 from tests.test_gpu_parity import assert_close, say
-from workloads import config, make_case, multi_canvas_structure
+from workloads import config, make_case, multi_canvas_structure, with_positions
 from workloads.device import DeviceCase
 
 pytestmark = pytest.mark.gpu
@@ -31,14 +31,8 @@ def canvas_case(seed, batch=3, prompt=40, canvas=24, n_canvas=3, G=4, Hkv=2, d=1
 
 
 def positions(case, live_pos, com_pos):
-    """q_pos [total_q] and kv_pos [num_pages*P] (fixture: committed row j of sequence s sits in
-    page page_table[s, j//P], slot j%P; unused slots hold a position nobody is near)."""
-    q_pos = np.concatenate([np.asarray(p, np.int32) for p in live_pos] + [np.zeros(0, np.int32)])
-    kv_pos = np.full(case.num_pages * case.page_size, -(10 ** 6), np.int32)
-    for s, cp in enumerate(com_pos):
-        for j, p in enumerate(cp):
-            kv_pos[case.page_table[s, j // case.page_size] * case.page_size + j % case.page_size] = p
-    return q_pos, kv_pos
+    with_positions(case, live_pos, com_pos)
+    return case.q_pos, case.kv_pos
 
 
 def run(case, q_pos, kv_pos, window, plan=True, tile=None):
@@ -92,8 +86,7 @@ def test_mode_B_window_small(spec):
 def test_mode_B_window_tile_classes(seed, W, tq, tk, shape):
     case, (q_pos, kv_pos) = canvas_case(seed, G=4, d=64, P=8, **shape)
     dc = DeviceCase(case)
-    meta = bcp.StepMeta(**dc.meta_kwargs(), tile_q=tq, tile_k=tk, check=True, window=W,
-                        q_pos=torch.from_numpy(q_pos).cuda(), kv_pos=torch.from_numpy(kv_pos).cuda())
+    meta = bcp.StepMeta(**dict(dc.meta_kwargs(), tile_q=tq, tile_k=tk, check=True, window=W))
     nqt, nkt = bcp.num_q_tiles(meta), bcp.num_k_tiles(meta)
     tc = torch.full((case.batch, nqt, nkt), 255, dtype=torch.uint8, device="cuda")
     bcp.build_tile_mask(meta, tile_class=tc)
@@ -107,14 +100,8 @@ def test_mode_B_window_tile_classes(seed, W, tq, tk, shape):
 def test_C4_multi_canvas_window_sampled():
     # C4's multi-canvas layout with its positions, W = 512: canvases far from the prompt's
     # start lose its early part.
-    rng = np.random.default_rng(1004)   # the seed config(4) uses, so the structure is C4's
-    inv = 1.0 / np.sqrt(128.0)
-    ql, kl, qb, kb, live_pos, com_pos = multi_canvas_structure(rng, 16, 1024, 256, 3)
-    case = make_case(1004, name="C4", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
-                     page_size=16, q_lens=ql, kv_lens=kl, q_blk_seqs=qb, kv_blk_seqs=kb, qkv_std=inv, rng=rng)
-    ref_case = config(4)
-    assert np.array_equal(case.q_lens, ref_case.q_lens) and np.array_equal(case.kv_len, ref_case.kv_len)
-    q_pos, kv_pos = positions(case, live_pos, com_pos)
+    case = config(4)
+    q_pos, kv_pos = case.q_pos, case.kv_pos
     rows = {s: np.unique(np.concatenate([[0, int(case.q_lens[s]) - 1], np.random.default_rng(s).integers(
         0, int(case.q_lens[s]), 10)])) for s in (0, 5, 15)}
     O_ref, L_ref = oracle_attention(case, rows=rows, window=512, q_pos=q_pos, kv_pos=kv_pos)

@@ -70,6 +70,10 @@ class Case:
     # Mode B structure in logical row order, per sequence (what the page placement used).
     q_blk_seqs: Optional[list] = None
     kv_blk_seqs: Optional[list] = None
+    # Absolute positions (multi-canvas layout), when the workload has them: per live row and
+    # per cache slot (unused slots hold a position far from every row).
+    q_pos: Optional[np.ndarray] = None
+    kv_pos: Optional[np.ndarray] = None
 
     @property
     def total_q(self) -> int:
@@ -303,7 +307,20 @@ def multi_canvas_structure(rng: np.random.Generator, batch: int, prompt: int, ca
 
 
 def _multi_canvas(seed: int, rng: np.random.Generator, std: float) -> Case:
-    q_lens, kv_lens, qb, kb, _, _ = multi_canvas_structure(rng, 16, 1024, 256, 3)
-    return make_case(seed, name="C4", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+    q_lens, kv_lens, qb, kb, live_pos, com_pos = multi_canvas_structure(rng, 16, 1024, 256, 3)
+    case = make_case(seed, name="C4", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
                      block_size=256, page_size=16, q_lens=q_lens, kv_lens=kv_lens, q_blk_seqs=qb,
                      kv_blk_seqs=kb, qkv_std=std, rng=rng, desc=CONFIG_NAMES[4])
+    return with_positions(case, live_pos, com_pos)
+
+
+def with_positions(case: Case, live_pos, com_pos) -> Case:
+    """Attach q_pos [total_q] and kv_pos [num_pages*P]: committed row j of sequence s sits in
+    page page_table[s, j//P], slot j%P, as its block id does."""
+    case.q_pos = np.concatenate([np.asarray(p, np.int32) for p in live_pos] + [np.zeros(0, np.int32)])
+    kv_pos = np.full(case.num_pages * case.page_size, -(10 ** 6), np.int32)
+    for s, cp in enumerate(com_pos):
+        for j, p in enumerate(cp):
+            kv_pos[case.page_table[s, j // case.page_size] * case.page_size + j % case.page_size] = p
+    case.kv_pos = kv_pos
+    return case

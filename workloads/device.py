@@ -25,6 +25,7 @@ class DeviceCase:
         self.k_cache, self.v_cache = data(case.k_cache), data(case.v_cache)
         self.cu_q, self.kv_len, self.page_table = ints(case.cu_q), ints(case.kv_len), ints(case.page_table)
         self.q_blk, self.kv_blk = ints(case.q_blk), ints(case.kv_blk)
+        self.q_pos, self.kv_pos = ints(case.q_pos), ints(case.kv_pos)
 
     def meta_kwargs(self):
         c = self.case
@@ -33,7 +34,7 @@ class DeviceCase:
                     cu_q=self.cu_q, kv_len=self.kv_len, page_table=self.page_table,
                     num_pages=c.num_pages, page_size=c.page_size, total_q=c.total_q,
                     max_q_len=c.max_q_len, max_kv_len=c.max_kv_len, q_blk=self.q_blk,
-                    kv_blk=self.kv_blk)
+                    kv_blk=self.kv_blk, q_pos=self.q_pos, kv_pos=self.kv_pos)
 
 
 def to_host_bits(t):
