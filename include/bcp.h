@@ -104,7 +104,10 @@ typedef struct bcp_meta {
   int32_t page_size;           /* P >= 1 */
   int32_t max_pages_per_seq;   /* row stride of page_table */
   int32_t max_kv_len;          /* host bound on kv_len[s] */
-  int32_t tile_q;              /* query positions per q-tile; 0 -> 256/(Hq/Hkv) */
+  int32_t tile_q;              /* query positions per q-tile; 0 -> 256/(Hq/Hkv), or 64/(Hq/Hkv)
+                                  for bf16 steps with max_q_len*(Hq/Hkv) <= 64 (short live
+                                  blocks such as a causal extend: "Introspective Diffusion
+                                  Language Models" summary page, serving section) */
   int32_t tile_k;              /* keys per k-tile; 0 -> 64 */
   uint32_t flags;              /* BCP_F_CHECK | BCP_F_LIVE_IN_CACHE */
   int32_t window;              /* sliding window W >= 1 in positions, or 0 for none: key
@@ -146,7 +149,7 @@ size_t bcp_plan_size(const bcp_meta* m);
  *               page_size > tile_k there is one entry per tile: the page of its first row.
  *   plan        [bcp_plan_size(m) bytes], or NULL: the step plan for attn_block_causal_paged
  *               (per q-tile list of non-skipped key tiles and a balanced split-KV work
- *               list). Only valid for the attention tile sizes (tile_q = 256/(Hq/Hkv),
+ *               list). Only valid for the attention tile sizes (tile_q = the default,
  *               tile_k = 64) and only for metadata identical to the attention call's.
  * At least one output must be non-NULL. Errors: BCP_E_ARG, BCP_E_WORKSPACE (plan_bytes too
  * small), BCP_E_RANGE (checked mode), BCP_E_HIP.
@@ -174,8 +177,8 @@ size_t attn_block_causal_paged_workspace_size(const bcp_meta* m);
  *   stats       uint64[4] or NULL: counters incremented by this call -- FULL tiles
  *               computed, PARTIAL tiles computed, SKIP tiles not loaded (each per kv head),
  *               K/V bytes loaded.
- * Supported: head_dim 64/128; bf16 (MFMA path) or f32 (vector path); tile_q and tile_k
- * must equal their defaults. Every row must see at least one key (always true: a live row
+ * Supported: head_dim 64/128; bf16 (MFMA path: 256 packed query rows per work item, or 64
+ * for the narrow default) or f32 (vector path); tile_q and tile_k must equal their defaults. Every row must see at least one key (always true: a live row
  * sees itself); a row that sees none gets out = 0 and lse = -inf.
  * Errors: BCP_E_ARG, BCP_E_UNSUPPORTED, BCP_E_WORKSPACE, BCP_E_RANGE (checked), BCP_E_HIP.
  */
