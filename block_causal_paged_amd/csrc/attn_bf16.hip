@@ -843,18 +843,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 // short causal extend of up to 16 positions at four query heads per kv head.
 //
 // With so few live rows the wide kernel's 256-row work items would be mostly padding while
-// each key tile still costs the full matrix and softmax work. Here a workgroup of two waves
-// owns an item of 64 packed rows (32 per wave, each on its own SIMD). For each key tile each
-// wave stages four of its eight 8-row runs into a ring of kNStages stages, then computes
-// S = K Q^T, the mask and online softmax, and O += V P for its 32 rows. Loads run kNLead
-// tiles ahead; one barrier per tile publishes the tile (each wave has waited for its own
-// loads of it) and, since a wave passes it only after finishing the previous tile, also
-// frees the stage the next loads overwrite (kNLead + 2 <= kNStages).
-constexpr int kNWaves = 2, kNThreads = 64 * kNWaves;
-constexpr int kNStages = 4, kNLead = 2;
-constexpr int kNRuns = kWaves / kNWaves;            // 8-row runs each wave stages per tile
+// each key tile still costs the full matrix and softmax work. Here a workgroup of four waves
+// owns an item of 64 packed rows. The waves form two teams of two (one wave per SIMD), each
+// wave of a team holding 32 rows; team p computes the tiles p, p+2, p+4, ... of each window
+// with its own online-softmax state, so two tiles are in work at once, and team 1's state is
+// merged into team 0's at the end. Every wave stages two of each tile's eight 8-row runs into
+// a ring of four stages, one pair of tiles ahead of the pair in work: a barrier before a
+// pair's loads frees the two stages they overwrite (every wave is done with the pair before),
+// and one after them publishes the pair in work (each wave has waited for its own loads).
+constexpr int kNWaves = 4, kNThreads = 64 * kNWaves;
+constexpr int kNStages = 4;                           // two pairs of tiles
+constexpr int kNRuns = kWaves / kNWaves;              // 8-row runs each wave stages per tile
 constexpr int kNWinPerThread = kWin * kWaves / kNThreads;
-static_assert(kNLead == 2 && kNLead + 2 <= kNStages, "a stage is reused only after both waves left it");
 
 template <int HD>
 struct NarrowSmem {
@@ -884,13 +884,13 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16, NDB = HD / 32;
-  // Loads in flight per wave stay within the 6-bit counter: three tiles of at most
-  // kNRuns * (2*NI + 1) each, or, when positions are staged too (2*NI + 2 per run), two.
-  static_assert((kNLead + 1) * kNRuns * (2 * NI + 1) <= 63 && kNLead * kNRuns * (2 * NI + 2) <= 63, "vmcnt range");
+  // Loads in flight per wave stay within the 6-bit counter: two pairs of tiles.
+  static_assert(4 * kNRuns * (2 * NI + 2) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) NarrowSmem<HD> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hl = lane >> 5;
+  const int team = uni(wave) >> 1;           // computes tiles team, team + 2, ... of a window
   const int G = a.G;
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
@@ -901,7 +901,7 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
   const int ta = (lane & 15) >> 2, tc = lane & 3;
   const int vrow0 = 4 * hl + ta;
   const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * tc;
-  const int rho = wave * 32 + col;           // this lane's packed query row
+  const int rho = (wave & 1) * 32 + col;     // this lane's packed query row (in either team)
   int koff[NT], voff[NDB];
   {
     const int sw = kswz<HD>(col);
@@ -989,7 +989,7 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
     float m = -INFINITY, l = 0.f;
-    int n_partial = 0;
+    int n_partial = 0, n_mine = 0;
 
     for (int wb = ob; wb < oe; wb += kWin) {
       const int nt = min(oe - wb, kWin);
@@ -1003,7 +1003,7 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
       }
       __syncthreads();
 
-      // This wave's four runs of tile x into stage x % kNStages; returns the loads issued.
+      // This wave's two runs of tile x into stage x % kNStages; returns the loads issued.
       auto fetch = [&](int x) {
         int n = 0;
 #pragma unroll
@@ -1014,24 +1014,20 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
         }
         return n;
       };
-      // c2, c3: this wave's loads of tiles t+1 and t+2 (kNLead = 2).
       fetch(0);
-      int c2 = fetch(1);
-      int e_next = sm.win_e[0];
-      for (int t = 0; t < nt; ++t) {
-        int c3;
-        if constexpr (BAND_B) {   // positions staged: land tile t before issuing more
-          wait_vm_in<0, 63>(c2);
-          c3 = t + kNLead < nt ? fetch(t + kNLead) : 0;
-        } else {
-          c3 = t + kNLead < nt ? fetch(t + kNLead) : 0;
-          wait_vm_in<0, 63>(c2 + c3);    // this wave's loads of tile t have landed
-        }
-        const int e_t = uni(e_next);
-        __syncthreads();               // and the other wave's; both left tile t-1
-        e_next = sm.win_e[min(t + 1, kWin - 1)];
-        c2 = c3;
+      fetch(1);
+      for (int k = 0; 2 * k < nt; ++k) {
+        __syncthreads();               // every wave is done with pair k-1: its stages are free
+        int cnext = 0;                 // this wave's loads of pair k+1
+        if (2 * k + 2 < nt) cnext += fetch(2 * k + 2);
+        if (2 * k + 3 < nt) cnext += fetch(2 * k + 3);
+        wait_vm_in<0, 63>(cnext);      // this wave's loads of pair k have landed
+        __syncthreads();               // and every other wave's
+        const int t = 2 * k + team;
+        if (t >= nt) continue;         // an odd last tile: team 1 has none
+        const int e_t = uni(sm.win_e[t]);
         const int st_ = t % kNStages;
+        ++n_mine;
 
         // S^T = K Q^T for this wave's 32 rows (two 32-key blocks).
         f32x16 sc[2];
@@ -1130,11 +1126,41 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
       }
     }   // window
 
-    // Epilogue: lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4 of row rho.
+    // Merge team 1's state into team 0's through LDS (the ring is free once every wave has
+    // passed this barrier): both teams hold the same rows in the same lane layout.
+    __syncthreads();
+    {
+      constexpr int XW = NDB * 16 + 2;   // floats per lane: O, m, l
+      float* xb = (float*)&sm.k[0][0] + ((wave & 1) * 64 + lane) * XW;
+      if (team == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) xb[16 * db + v] = o[db][v];
+        xb[NDB * 16] = m;
+        xb[NDB * 16 + 1] = l;
+      }
+      __syncthreads();
+      if (team == 0) {
+        const float m1 = xb[NDB * 16], l1 = xb[NDB * 16 + 1];
+        const float M = fmaxf(m, m1);
+        const float a0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        const float a1 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a0 + xb[16 * db + v] * a1;
+        l = l * a0 + l1 * a1;
+        m = M;
+      }
+    }
+
+    // Epilogue (team 0): lane (col, hl) of block db holds d = 32db + 8(v/4) + 4hl + v%4 of
+    // row rho.
     const float lt = l + __shfl_xor(l, 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
-    if (qvalid) {
+    if (qvalid && team == 0) {
       if (pslot < 0) {
         const int64_t row = (int64_t)(it.q0 + pos) * a.Hq + (int64_t)it.g * G + hh;
         uint16_t* op = (uint16_t*)a.out + row * HD + 4 * hl;
@@ -1158,11 +1184,10 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
         if (hl == 0) a.part_lse[(int64_t)pslot * kRowsPerWG + rho] = lse2;
       }
     }
-    if (a.stats && tid == 0) {
-      const int n = oe - ob;
-      atomicAdd(&a.stats[0], (unsigned long long)(n - n_partial));
+    if (a.stats && (tid & 127) == 0) {   // the first wave of each team, for its tiles
+      atomicAdd(&a.stats[0], (unsigned long long)(n_mine - n_partial));
       atomicAdd(&a.stats[1], (unsigned long long)n_partial);
-      atomicAdd(&a.stats[3], (unsigned long long)n * 2ull * kTileK * HD * 2ull);
+      if (team == 0) atomicAdd(&a.stats[3], (unsigned long long)(oe - ob) * 2ull * kTileK * HD * 2ull);
     }
   }
 }
