@@ -75,8 +75,9 @@ int check_meta(const bcp_meta* m, Geo* g) {
   if ((int64_t)m->max_kv_len > (int64_t)m->max_pages_per_seq * m->page_size)
     return fail(BCP_E_ARG, "max_kv_len %d exceeds max_pages_per_seq * page_size", m->max_kv_len);
   if (m->flags & ~(BCP_F_CHECK | BCP_F_LIVE_IN_CACHE)) return fail(BCP_E_ARG, "unknown flags 0x%x", m->flags);
-  if ((int64_t)m->num_pages * m->page_size > INT32_MAX || (int64_t)m->batch * m->max_pages_per_seq > INT32_MAX)
-    return fail(BCP_E_ARG, "pool or page table too large for 32-bit slot indices");
+  if ((int64_t)m->num_pages * m->page_size > INT32_MAX || (int64_t)m->batch * m->max_pages_per_seq > INT32_MAX ||
+      (int64_t)m->max_pages_per_seq * m->page_size > INT32_MAX)
+    return fail(BCP_E_ARG, "pool, page table or per-sequence capacity too large for 32-bit row indices");
   if (m->window < 0) return fail(BCP_E_ARG, "window must be >= 0 (got %d)", m->window);
   if (m->window > 0 && m->q_blk && (!m->q_pos || !m->kv_pos))
     return fail(BCP_E_ARG, "a sliding window in mode B needs q_pos and kv_pos");

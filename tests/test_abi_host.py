@@ -79,6 +79,8 @@ def test_geometry_queries():
     (dict(window=-1), bcp.BCP_E_ARG),
     (dict(flags=4), bcp.BCP_E_ARG),                       # unknown flag
     (dict(window=256, q_blk=FAKE, kv_blk=FAKE), bcp.BCP_E_ARG),     # window in mode B needs positions
+    (dict(batch=1, total_q=64, max_pages_per_seq=1 << 21, page_size=2048, num_pages=16),
+     bcp.BCP_E_ARG),                                       # 2^32 rows per sequence: past 32-bit rows
 ])
 def test_attention_rejects_bad_meta(over, code):
     assert attn(meta(**over)) == code
