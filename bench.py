@@ -32,7 +32,9 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 FP32_PEAK_TFLOPS = 157.3
 # Which roof binds each workload (algorithmic FLOP/byte against the 314.6 FLOP/B ridge).
 BOUND = {1: "hbm", 2: "hbm", 3: "mfma", 4: "mfma", 5: "hbm", 6: "hbm"}
-KERNEL_SOURCES = ["attn_bf16.hip", "combine.hip"]
+# Sources whose code decides the attention call's memory traffic: the kernels, the planner
+# that lays out their work, and the launch set-up.
+KERNEL_SOURCES = ["attn_bf16.hip", "combine.hip", "tiles.hip", "abi.cpp"]
 LAYERS = 32   # layers of the model step that is also timed as a captured graph
 
 
@@ -51,6 +53,10 @@ def parse():
     p.add_argument("--live-in-cache", action="store_true",
                    help="live keys/values already in the pool at kv_len + i: attention reads one "
                         "paged source and the commit moves only block ids")
+    p.add_argument("--also", default="4,5",
+                   help="comma-separated workloads whose attention call is also timed (cold, with its "
+                        "own roofline) on the default line; '' for none")
+    p.add_argument("--also-steps", type=int, default=20, help="timed calls per --also workload")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, then WRITE_SIZE) of `bench.py --calib-copy` into "
@@ -201,12 +207,21 @@ def traffic_from_profile(cfg):
 def cpu_baseline(case, budget_s, window=0):
     """The oracle as it stands, over whole sequences of the same workload in order, pass
     after pass, until the budget is spent; scaled to microseconds per full step by the
-    number of query rows covered."""
+    number of query rows covered. The BLAS pool is held to the cores this process may run
+    on (its affinity mask), or to the pool's own size if that is smaller (the share a job
+    is given), and `cores` reports that count."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    affinity = len(os.sched_getaffinity(0))
+    pool = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    threads = max(1, min(affinity, pool))
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline_run(case, budget_s, window, threads, affinity, oracle, np)
+
+
+def _cpu_baseline_run(case, budget_s, window, threads, affinity, oracle, np):
     t0 = time.perf_counter()
     rows_done = 0
     seqs = 0
@@ -228,8 +243,75 @@ def cpu_baseline(case, budget_s, window=0):
     what = (f"{seqs // case.batch} full passes over the {case.batch} sequences" + (f" and {seqs % case.batch} more"
             if seqs % case.batch else "")) if seqs >= case.batch else f"sequences 0..{seqs - 1} of {case.batch}"
     return {"value": per_step_us, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "affinity_cores": affinity,
             "sample": f"float64 NumPy oracle, all heads, on {what} ({steps:.3g} steps of query rows) "
-                      f"in {dt:.1f} s, scaled to one step"}
+                      f"in {dt:.1f} s on {threads} BLAS threads, scaled to one step"}
+
+
+def roofline_of(case, cfg, attn_us_mean, window=0):
+    """(roofline dict without traffic, useful flops, cached/live K/V bytes, Q+O bytes)."""
+    flops, cached_kv, live_kv, q_o = workload_stats(case, window)
+    algo_bytes = cached_kv + live_kv + q_o
+    bound = BOUND[cfg]
+    if bound == "hbm":
+        achieved, peak, unit = algo_bytes / (attn_us_mean * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        peak = MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else FP32_PEAK_TFLOPS
+        achieved, unit = flops / (attn_us_mean * 1e-6) / 1e12, "TFLOP/s"
+    G = case.num_q_heads // case.num_kv_heads
+    narrow = case.dtype == "bf16" and 64 % G == 0 and case.max_q_len * G <= 64
+    kern = "attn_f32_kernel" if case.dtype != "bf16" else ("attn_bf16_narrow_kernel" if narrow else "attn_bf16_kernel")
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "kernel": f"attn_block_causal_paged ({kern} + combine_kernel)",
+            "algorithmic_bytes": algo_bytes, "useful_flops": flops, "launch_us_mean": round(attn_us_mean, 3)}
+    return roof, flops, cached_kv, live_kv, q_o
+
+
+def measure_attention_only(cfg, steps, flush):
+    """Cold attention calls of workload `cfg` (flush outside the events), with the roofline of
+    the mean: the figure every gated workload gets on the default line."""
+    import numpy as np
+    import torch
+
+    import block_causal_paged_amd as bcp
+    from workloads import CONFIG_NAMES, config
+    from workloads.device import DeviceCase
+
+    case = config(cfg)
+    dc = DeviceCase(case)
+    meta = bcp.StepMeta(**dc.meta_kwargs())
+    plan = torch.empty(bcp.plan_size(meta), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, bcp.attn_workspace_size(meta)), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dc.q)
+    bcp.build_tile_mask(meta, plan=plan)
+
+    def call():
+        bcp.attn_block_causal_paged(meta, dc.q, dc.k_new, dc.v_new, dc.k_cache, dc.v_cache, out, plan=plan,
+                                    workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        flush.fill_(k & 0xFF)
+        evs[k][0].record()
+        call()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    roof, flops, cached_kv, live_kv, _ = roofline_of(case, cfg, float(us.mean()))
+    roof["traffic"] = traffic_from_profile(cfg)
+    rec = {"workload": f"C{cfg} {CONFIG_NAMES[cfg]}",
+           "attention_us": {"median": round(float(np.median(us)), 3), "mean": round(float(us.mean()), 3),
+                            "p10": round(float(np.percentile(us, 10)), 3),
+                            "p90": round(float(np.percentile(us, 90)), 3), "calls": steps},
+           "useful_tflops": round(flops / (us.mean() * 1e-6) / 1e12, 2),
+           "kv_gbps": round((cached_kv + live_kv) / (us.mean() * 1e-6) / 1e9, 1),
+           "roofline": roof}
+    del dc, plan, ws, out
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -390,20 +472,11 @@ def main():
             torch.mul(src, 1.0, out=dst_buf)
         torch.cuda.synchronize()
 
-    flops, cached_kv, live_kv, q_o = workload_stats(case, args.window)
-    G = case.num_q_heads // case.num_kv_heads
-    narrow = case.dtype == "bf16" and 64 % G == 0 and case.max_q_len * G <= 64
-    attn_kernel = "attn_f32_kernel" if case.dtype != "bf16" else ("attn_bf16_narrow_kernel" if narrow else "attn_bf16_kernel")
-    algo_bytes = cached_kv + live_kv + q_o
     a_med = float(np.median(attn_us))
     a_mean = float(np.mean(attn_us))
-    bound = BOUND[cfg]
-    if bound == "hbm":
-        achieved, peak, unit = algo_bytes / (a_mean * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        peak = MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else FP32_PEAK_TFLOPS
-        achieved, unit = flops / (a_mean * 1e-6) / 1e12, "TFLOP/s"
-    traffic = None if args.window or args.live_in_cache else traffic_from_profile(cfg)
+    roof, flops, cached_kv, live_kv, q_o = roofline_of(case, cfg, a_mean, args.window)
+    algo_bytes = cached_kv + live_kv + q_o
+    roof["traffic"] = None if args.window or args.live_in_cache else traffic_from_profile(cfg)
 
     rec = {
         "metric": METRIC,
@@ -425,12 +498,7 @@ def main():
                    "block_size": case.block_size, "mode": case.mode,
                    **({"window": args.window} if args.window else {}),
                    **({"live_in_cache": True} if args.live_in_cache else {})},
-        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4),
-                     "traffic": traffic,
-                     "kernel": f"attn_block_causal_paged ({attn_kernel} + combine_kernel)",
-                     "algorithmic_bytes": algo_bytes, "useful_flops": flops,
-                     "launch_us_mean": round(a_mean, 3)},
+        "roofline": roof,
         "attention_us": {"median": round(a_med, 3), "mean": round(a_mean, 3),
                          "p10": round(float(np.percentile(attn_us, 10)), 3),
                          "p90": round(float(np.percentile(attn_us, 90)), 3),
@@ -448,6 +516,13 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    also = [int(x) for x in args.also.split(",") if x.strip()] if not (args.window or args.live_in_cache) else []
+    also = [c for c in also if c != cfg]
+    if also:
+        # The other gated workloads' attention calls, each cold and with its own roofline.
+        del dc, ws, out, plan
+        torch.cuda.empty_cache()
+        rec["other_workloads"] = {f"C{c}": measure_attention_only(c, args.also_steps, flush) for c in also}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, args.window)
     print(json.dumps(rec))

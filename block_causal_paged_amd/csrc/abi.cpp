@@ -135,8 +135,10 @@ int refuse_if_capturing(hipStream_t stream) {
   return BCP_OK;
 }
 
-// Checked mode: the metadata the kernels will read, validated on the host.
-int validate_metadata(const bcp_meta* m, hipStream_t stream) {
+// Checked mode: the metadata the kernels will read, validated on the host. *len_hash (when
+// given) receives the hash of the sequences' live rows and committed lengths that the
+// planner records in a plan's header.
+int validate_metadata(const bcp_meta* m, hipStream_t stream, uint32_t* len_hash = nullptr) {
   if (int rc = refuse_if_capturing(stream)) return rc;
   std::vector<int32_t> cu, kvl, pt, qb, kb;
   int rc;
@@ -180,6 +182,37 @@ int validate_metadata(const bcp_meta* m, hipStream_t stream) {
   for (int i = 0; i < (int)qb.size(); ++i)
     if (qb[i] == kNegInfBlk || qb[i] >= kNoKeyBlk - 1)
       return fail(BCP_E_RANGE, "q_blk[%d] is a reserved value", i);
+  if (len_hash) {
+    const int64_t cap = (int64_t)m->max_pages_per_seq * m->page_size;
+    uint32_t h = 0;
+    for (int s = 0; s < m->batch; ++s)
+      h += seq_len_hash(s, cu[s], cu[s + 1] - cu[s], (int)std::min<int64_t>(kvl[s], cap));
+    *len_hash = h;
+  }
+  return BCP_OK;
+}
+
+// Checked mode: a caller's plan must have been built by build_tile_mask for this step --
+// the same shapes, window and mode, and the same live rows and committed lengths.
+int validate_plan(const bcp_meta* m, const Geo& g, const void* plan, uint32_t len_hash, hipStream_t stream) {
+  int32_t h[kHdrWords];
+  hipError_t e = hipMemcpyAsync(h, plan, sizeof h, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "checked mode: reading the plan header");
+  if (h[kHdrMagic] != kPlanMagic) return fail(BCP_E_ARG, "plan was not written by build_tile_mask");
+  if (h[kHdrTileQ] != g.tq || h[kHdrTileK] != g.tk || h[kHdrNqt] != g.nqt || h[kHdrNkt] != g.nkt ||
+      h[kHdrBatch] != m->batch || h[kHdrHkv] != m->num_kv_heads || h[kHdrWindow] != m->window ||
+      h[kHdrModeB] != (g.mode_b ? 1 : 0) || h[kHdrTotalQ] != m->total_q ||
+      h[kHdrKvCap] != m->max_pages_per_seq * m->page_size)
+    return fail(BCP_E_ARG,
+                "plan was built for another step shape (plan: batch %d, Hkv %d, tiles %dx%d, grid %dx%d, "
+                "window %d, mode %s, total_q %d, capacity %d; meta: batch %d, Hkv %d, tiles %dx%d, grid %dx%d, "
+                "window %d, mode %s, total_q %d, capacity %d)",
+                h[kHdrBatch], h[kHdrHkv], h[kHdrTileQ], h[kHdrTileK], h[kHdrNqt], h[kHdrNkt], h[kHdrWindow],
+                h[kHdrModeB] ? "B" : "A", h[kHdrTotalQ], h[kHdrKvCap], m->batch, m->num_kv_heads, g.tq, g.tk,
+                g.nqt, g.nkt, m->window, g.mode_b ? "B" : "A", m->total_q, m->max_pages_per_seq * m->page_size);
+  if ((uint32_t)h[kHdrLenHash] != len_hash)
+    return fail(BCP_E_ARG, "plan was built for other live rows or committed lengths (a stale plan?)");
   return BCP_OK;
 }
 
@@ -260,6 +293,8 @@ int run_classify_and_plan(const bcp_meta* m, const Geo& g, uint8_t* tile_class, 
   p.total_q = m->total_q;
   p.max_q_len = m->max_q_len;
   p.kv_cap = m->max_pages_per_seq * m->page_size;
+  p.window = m->window;
+  p.mode_b = g.mode_b ? 1 : 0;
   hipError_t e = launch_classify(a, stream);
   if (e != hipSuccess) return hip_fail(e, "launch classify");
   if (plan) {
@@ -387,7 +422,9 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
     return fail(BCP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   if (workspace && !aligned(workspace, 16)) return fail(BCP_E_ARG, "workspace must be 16-byte aligned");
   if (m->flags & BCP_F_CHECK) {
-    if ((rc = validate_metadata(m, stream))) return rc;
+    uint32_t len_hash = 0;
+    if ((rc = validate_metadata(m, stream, &len_hash))) return rc;
+    if (plan && (rc = validate_plan(m, g, plan, len_hash, stream))) return rc;
   }
   g_err.clear();
   if (m->total_q == 0 || g.nqt == 0) return BCP_OK;

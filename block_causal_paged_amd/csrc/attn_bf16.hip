@@ -220,11 +220,14 @@ struct FastOffsets {
 // `sk` and value stage `sv`: NI K and NI V wave instructions, plus one block-id copy for
 // partial mode-B tiles. Returns the number of loads issued. When the run's 8 rows are
 // present and consecutive in memory (row0 >= 0), one wave-uniform base and fixed per-lane
-// offsets (fo, made for a run of the same parity) address them. Otherwise each lane resolves its own row through the page table, and an
-// absent key (past its region's length, or in a page outside the pool) copies the
-// sequence's first live row (its first query row when the live rows are read from the
-// pool): absent keys only occur in partial tiles, where the mask gives them weight exactly
-// 0, and that row is finite, so it adds exactly nothing.
+// offsets (fo, made for a run of the same parity) address them. Otherwise each lane
+// resolves its own row through the page table, and a key past its region's length copies
+// the sequence's first live row (its first query row when the live rows are read from the
+// pool): such keys only occur in partial tiles, where the mask gives them weight exactly 0,
+// and that row is finite, so they add exactly nothing. A key whose page id lies outside the
+// pool (invalid metadata, which checked mode rejects) is loaded from that same row so that
+// no load leaves the buffers; it keeps its place in the softmax, so the result for such
+// input is unspecified.
 template <int HD, int NI, bool BAND_B, class Smem>
 __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st, Smem& sm,
                                            int sk, int sv, const FastOffsets<HD>& fo, int q) {
@@ -309,9 +312,10 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
     if (!a.mode_b) {
       if (lane < 8) sm.kblk[sv][r] = r >= nvalid ? kNoKeyBlk : (cached ? kNegInfBlk : j / a.block_size);
     } else {
-      // Keys that exist take their id from memory (a key in a page outside the pool gets
-      // the sequence's first live row's id: its K and V were substituted by that row, so
-      // it adds exactly nothing whatever its weight); absent keys get the id nobody sees.
+      // Keys that exist take their id from memory; absent keys get the id nobody sees. A
+      // key in a page outside the pool (invalid metadata; its K and V were replaced by the
+      // sequence's first live row) reads that row's id instead, so no load leaves the
+      // buffers; the result for such input is unspecified.
       if constexpr (!BAND_B) {
         const int32_t* src = a.q_blk + it.q0;
         if (r < nvalid) {
@@ -452,8 +456,15 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
   // The range's record holds its item bounds and a copy of its first item.
-  cint32* rec = plan + L.rng + kRngWords * range_of_wg(blockIdx.x);
+  cint32* rec = plan + L.rng + kRngWords * range_of_wg(blockIdx.x);   // in bounds for any plan
   const int w_begin = rec[0], w_end = rec[1];
+  {
+    // The record and the header arrive in one round trip; the check follows.
+    PlanShape h = plan_shape(plan);
+    asm volatile("" : "+s"(h.w[0]), "+s"(h.w[1]), "+s"(h.w[2]), "+s"(h.w[3]), "+s"(h.w[4]), "+s"(h.w[5]), "+s"(h.w[6]),
+                 "+s"(h.w[7]), "+s"(h.w[8]), "+s"(h.w[9]), "+s"(h.w[10]), "+s"(h.w[11]) : "s"(w_begin), "s"(w_end));
+    if (!plan_matches(h, a)) return;
+  }
   const uint16_t* qg = (const uint16_t*)a.q;
   const float sl2 = a.scale_log2;
   // V transpose reads: lane (group g16 = lane/16, j = lane%16) is source lane 4*ta + tc of
@@ -492,13 +503,15 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   for (int item = w_begin; item < w_end; ++item) {
     Item it;
     cint32* ip = item == w_begin ? rec + 2 : plan + L.items + kItemWords * (int64_t)item;
-    const int u = ip[0], ob = ip[2], oe = ip[3], pslot = ip[4];
-    it.g = ip[1];
+    PlanItem pi;
+    read_item(ip, &pi);
+    const int u = pi.u, ob = pi.ob, oe = pi.oe, pslot = pi.pslot;
+    it.g = pi.g;
     it.s = u / a.nqt;
     const int r = u - it.s * a.nqt;
-    it.q0 = ip[5];       // the unit's live rows and committed length, as the planner
-    it.q_len = ip[6];    // clamped them
-    it.kvl = ip[7];
+    it.q0 = pi.q0;       // the unit's live rows and committed length, as the planner
+    it.q_len = pi.q_len; // clamped them
+    it.kvl = pi.kvl;
     it.lp_live = a.page_shift >= 0 ? it.kvl >> a.page_shift : it.kvl / a.page_size;
     const int i0 = r * a.tile_q;
     const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;
@@ -894,8 +907,15 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
   const int G = a.G;
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   cint32* plan = as_const(a.plan);
-  cint32* rec = plan + L.rng + kRngWords * range_of_wg(blockIdx.x);
+  cint32* rec = plan + L.rng + kRngWords * range_of_wg(blockIdx.x);   // in bounds for any plan
   const int w_begin = rec[0], w_end = rec[1];
+  {
+    // The record and the header arrive in one round trip; the check follows.
+    PlanShape h = plan_shape(plan);
+    asm volatile("" : "+s"(h.w[0]), "+s"(h.w[1]), "+s"(h.w[2]), "+s"(h.w[3]), "+s"(h.w[4]), "+s"(h.w[5]), "+s"(h.w[6]),
+                 "+s"(h.w[7]), "+s"(h.w[8]), "+s"(h.w[9]), "+s"(h.w[10]), "+s"(h.w[11]) : "s"(w_begin), "s"(w_end));
+    if (!plan_matches(h, a)) return;
+  }
   const uint16_t* qg = (const uint16_t*)a.q;
   const float sl2 = a.scale_log2;
   const int ta = (lane & 15) >> 2, tc = lane & 3;
@@ -930,13 +950,15 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
   for (int item = w_begin; item < w_end; ++item) {
     Item it;
     cint32* ip = item == w_begin ? rec + 2 : plan + L.items + kItemWords * (int64_t)item;
-    const int u = ip[0], ob = ip[2], oe = ip[3], pslot = ip[4];
-    it.g = ip[1];
+    PlanItem pi;
+    read_item(ip, &pi);
+    const int u = pi.u, ob = pi.ob, oe = pi.oe, pslot = pi.pslot;
+    it.g = pi.g;
     it.s = u / a.nqt;
     const int r = u - it.s * a.nqt;
-    it.q0 = ip[5];
-    it.q_len = ip[6];
-    it.kvl = ip[7];
+    it.q0 = pi.q0;
+    it.q_len = pi.q_len;
+    it.kvl = pi.kvl;
     it.lp_live = a.page_shift >= 0 ? it.kvl >> a.page_shift : it.kvl / a.page_size;
     const int i0 = r * a.tile_q;
     const int32_t* list = a.plan + L.list + (int64_t)u * a.nkt;

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int G = a.G;
   const PlanLayout L = plan_layout(a.batch, a.nqt, a.nkt, a.Hkv);
   const int rg = range_of_wg(blockIdx.x);
+  if (!plan_matches(as_const(a.plan), a)) return;
   const int w_begin = a.plan[L.wg + rg], w_end = a.plan[L.wg + rg + 1];
   const float* qg = (const float*)a.q;
   const float sl2 = a.scale_log2;
@@ -31,12 +32,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     atomicAdd(&a.stats[2], (unsigned long long)a.Hkv * ((unsigned long long)L.units * a.nkt - a.plan[3]));
 
   for (int item = w_begin; item < w_end; ++item) {
-    const int* ip = a.plan + L.items + kItemWords * (int64_t)item;
-    const int u = ip[0], g = ip[1], ob = ip[2], oe = ip[3], pslot = ip[4];
+    PlanItem pi;
+    read_item(as_const(a.plan) + L.items + kItemWords * (int64_t)item, &pi);
+    const int u = pi.u, g = pi.g, ob = pi.ob, oe = pi.oe, pslot = pi.pslot;
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
-    int q0, q_len;
-    live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
-    const int kvl = clampi(a.kv_len[s], 0, a.max_pages * a.page_size);
+    const int q0 = pi.q0, q_len = pi.q_len, kvl = pi.kvl;
     const int i0 = r * a.tile_q;
     const int* list = a.plan + L.list + (int64_t)u * a.nkt;
 

@@ -38,8 +38,21 @@ constexpr int kNegInfBlk = INT32_MIN;   // a committed row in mode A: seen by ev
 constexpr int kNoKeyBlk = INT32_MAX;    // an absent key: seen by nobody
 
 // Step plan, in int32 words:
-//   [0, 8)                  header: n_items, n_split, workgroups used, total tiles T, tile_q,
-//                           tile_k, nqt, nkt
+//   [0, 16)                 header (kHdr* below): n_items, n_split, workgroups used, total
+//                           tiles T, tile_q, tile_k, nqt, nkt, a magic word, batch, Hkv, a
+//                           hash of every sequence's live rows and committed length, the
+//                           window, mode B, total_q, the per-sequence capacity
+//                           max_pages_per_seq * page_size -- the attention and combine kernels
+//                           do nothing unless the shape words match their own arguments (every
+//                           item field the planner wrote then lies inside this call's
+//                           buffers), and checked mode compares the whole header with the meta
+//   rng   [kWGs][12]        per range: first item, end item, a copy of the first item's 8
+//                           words (when the range is not empty), 0, 0 -- so a workgroup
+//                           starts from one load; right after the header, at a place that
+//                           does not depend on the step's shape, so that a workgroup loads its
+//                           record together with the header and checks both at once
+//   split [kWGs][4]         unit, kv head, first partial slot, number of pieces (also at a
+//                           fixed place, for the combine kernel)
 //   cnt   [U]               non-skipped key tiles per unit (U = batch * nqt)
 //   list  [U * nkt]         per unit, its non-skipped virtual tile indices in order, each
 //                           stored as (t << 1) | is_partial; t < nct is cached tile t,
@@ -49,12 +62,33 @@ constexpr int kNoKeyBlk = INT32_MAX;    // an absent key: seen by nobody
 //   items [max_items][8]    unit, kv head, first ordinal, end ordinal, partial slot (-1 when
 //                           the item is a whole pair), and the unit's sequence's first live
 //                           row, live-row count and committed length (clamped to the pages)
-//   split [kWGs][4]         unit, kv head, first partial slot, number of pieces
-//   rng   [kWGs][12]        per range: first item, end item, a copy of the first item's 8
-//                           words (when the range is not empty), 0, 0 -- so a workgroup
-//                           starts from one load
 constexpr int kItemWords = 8;
 constexpr int kRngWords = 12;
+constexpr int kHdrWords = 16;
+enum {
+  kHdrItems = 0, kHdrSplit = 1, kHdrWgs = 2, kHdrTiles = 3, kHdrTileQ = 4, kHdrTileK = 5,
+  kHdrNqt = 6, kHdrNkt = 7, kHdrMagic = 8, kHdrBatch = 9, kHdrHkv = 10, kHdrLenHash = 11,
+  kHdrWindow = 12, kHdrModeB = 13, kHdrTotalQ = 14, kHdrKvCap = 15
+};
+constexpr int kPlanMagic = 0x32504342;   // "BCP2"
+
+// Hash of one sequence's live rows (first row q0, count ql) and committed length kvl, as the
+// planner clamps them; the plan header holds the wrapping sum over the sequences. It is
+// MurmurHash3's 32-bit finalizer applied in a chain, so a stale plan (one built before a
+// commit moved kv_len, say) is told apart from the current step in checked mode.
+__host__ __device__ inline uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+__host__ __device__ inline uint32_t seq_len_hash(int s, int q0, int ql, int kvl) {
+  uint32_t x = fmix32((uint32_t)s * 0x9E3779B1u ^ (uint32_t)q0);
+  x = fmix32(x ^ (uint32_t)ql * 0x27D4EB2Fu);
+  return fmix32(x ^ (uint32_t)kvl * 0x165667B1u);
+}
 
 struct PlanLayout {
   int64_t cnt, list, upre, wg, items, split, rng, words;
@@ -66,14 +100,14 @@ __host__ __device__ inline PlanLayout plan_layout(int batch, int nqt, int nkt, i
   p.units = batch * nqt;
   p.nkt = nkt;
   p.max_items = p.units * hkv + kWGs;
-  p.cnt = 8;
+  p.rng = kHdrWords;
+  p.split = p.rng + kRngWords * (int64_t)kWGs;
+  p.cnt = p.split + 4 * (int64_t)kWGs;
   p.list = p.cnt + p.units;
   p.upre = p.list + (int64_t)p.units * nkt;
   p.wg = p.upre + p.units + 1;
   p.items = p.wg + kWGs + 1;
-  p.split = p.items + kItemWords * (int64_t)p.max_items;
-  p.rng = p.split + 4 * (int64_t)kWGs;
-  p.words = p.rng + kRngWords * (int64_t)kWGs;
+  p.words = p.items + kItemWords * (int64_t)p.max_items;
   return p;
 }
 
@@ -100,6 +134,7 @@ struct PlanArgs {
   const int32_t* kv_len;
   int batch, nqt, nkt, num_kv_heads, tile_q, tile_k;
   int total_q, max_q_len, kv_cap;   // kv_cap = max_pages_per_seq * page_size
+  int window, mode_b;               // recorded in the header (with total_q and kv_cap)
 };
 
 struct AttnArgs {
@@ -194,6 +229,49 @@ __device__ __forceinline__ void live_rows(const int32_t* __restrict__ cu_q, int 
   const int a = clampi(cu_q[s], 0, total_q);
   *q0 = a;
   *q_len = clampi(cu_q[s + 1] - a, 0, min(max_q_len, total_q - a));
+}
+
+// True when the plan header describes the step these arguments describe (its shape words;
+// the length hash is compared on the host in checked mode). Every kernel that reads a plan
+// does nothing when it is false. When it is true, every field the planner wrote lies inside
+// this call's buffers: units, kv heads, tile ordinals and partial slots by the shape, the
+// live rows by total_q, the committed lengths by the per-sequence capacity.
+// h: header words kHdrTileQ .. kHdrKvCap, already loaded (so that a caller can load them
+// together with its range record).
+struct PlanShape {
+  int w[kHdrWords - kHdrTileQ];
+};
+__device__ __forceinline__ PlanShape plan_shape(cint32* plan) {
+  PlanShape h;
+#pragma unroll
+  for (int i = 0; i < kHdrWords - kHdrTileQ; ++i) h.w[i] = plan[kHdrTileQ + i];
+  return h;
+}
+__device__ __forceinline__ bool plan_matches(const PlanShape& h, const AttnArgs& a) {
+  auto w = [&](int k) { return h.w[k - kHdrTileQ]; };
+  return (w(kHdrMagic) == kPlanMagic) & (w(kHdrTileQ) == a.tile_q) & (w(kHdrTileK) == kTileK) &
+         (w(kHdrNqt) == a.nqt) & (w(kHdrNkt) == a.nkt) & (w(kHdrBatch) == a.batch) & (w(kHdrHkv) == a.Hkv) &
+         (w(kHdrWindow) == a.window) & (w(kHdrModeB) == a.mode_b) & (w(kHdrTotalQ) == a.total_q) &
+         (w(kHdrKvCap) == a.max_pages * a.page_size);
+}
+__device__ __forceinline__ bool plan_matches(cint32* plan, const AttnArgs& a) {
+  return plan_matches(plan_shape(plan), a);
+}
+
+// One work item of the plan: (unit, kv head, first and end tile ordinal, partial slot or
+// -1, the unit's sequence's first live row, live-row count and committed length).
+struct PlanItem {
+  int u, g, ob, oe, pslot, q0, q_len, kvl;
+};
+__device__ __forceinline__ void read_item(cint32* ip, PlanItem* it) {
+  it->u = ip[0];
+  it->g = ip[1];
+  it->ob = ip[2];
+  it->oe = ip[3];
+  it->pslot = ip[4];
+  it->q0 = ip[5];
+  it->q_len = ip[6];
+  it->kvl = ip[7];
 }
 #endif
 

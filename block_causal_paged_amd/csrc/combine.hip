@@ -29,11 +29,24 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   // depend on the live rows, and rows past the sequence's live rows are not stored.
   // Row groups per split: all NGRP for 256-row q-tiles, fewer for narrow ones.
   const int ngrp = min(NGRP, (a.tile_q * a.G + RPW - 1) / RPW);
+  // The first split record and the header arrive in one round trip (the records sit at a
+  // place that does not depend on the step's shape); the check follows.
+  bool ok;
+  {
+    PlanShape h = plan_shape(plan);
+    cint32* sp = plan + L.split + 4 * (int64_t)min((int)blockIdx.x / NGRP, kWGs - 1);   // the wide case's first
+    int r0 = sp[0], r1 = sp[1], r2 = sp[2], r3 = sp[3], ns = plan[kHdrSplit];
+    asm volatile("" : "+s"(r0), "+s"(r1), "+s"(r2), "+s"(r3), "+s"(ns), "+s"(h.w[0]), "+s"(h.w[1]), "+s"(h.w[2]),
+                 "+s"(h.w[3]), "+s"(h.w[4]), "+s"(h.w[5]), "+s"(h.w[6]), "+s"(h.w[7]), "+s"(h.w[8]), "+s"(h.w[9]),
+                 "+s"(h.w[10]), "+s"(h.w[11]));
+    ok = plan_matches(h, a);
+  }
+  if (!ok) return;
   for (int w = blockIdx.x; w < kWGs * ngrp; w += gridDim.x) {
     const int grp = w % ngrp, e = w / ngrp;
     cint32* sp = plan + L.split + 4 * (int64_t)e;   // inside the kWGs split records
     const int u = sp[0], g = sp[1], ps0 = sp[2], n = sp[3];
-    if (w >= plan[1] * ngrp) break;
+    if (w >= plan[kHdrSplit] * ngrp) break;
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
     const int rho = grp * RPW + rr;
     float lc[MAXC];

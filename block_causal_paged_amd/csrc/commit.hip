@@ -1,8 +1,9 @@
 // KV commit: finished rows copied bit for bit into their cache pages.
 //
-// "Inference for Interpretable Text-Diffusion Models", section "KV Cache": after a block is
-// fully unmasked, a final pass commits its keys and values to the cache; section "Paged
-// Attention": logical row j of sequence s lives in page page_table[s, j/P], slot j%P.
+// "Inference for Interpretable Text-Diffusion Models", section "KV Cache", step 3: the keys
+// and values of a block go to the cache in a pass of their own once all of its positions are
+// decided; section "Paged Attention": logical row j of sequence s lives in page
+// page_table[s, j/P], slot j%P.
 // "Inference: Fewer, smaller forwards", Advancement 11: arena entries carry their position
 // tag, recorded here as the block id next to the slot.
 //

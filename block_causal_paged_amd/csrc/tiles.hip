@@ -425,11 +425,23 @@ __device__ void plan_step(const PlanArgs& a) {
   const bool seq_lds = a.batch <= kPlanLdsSeqs;
   if (in_lds)
     for (int u = tid; u < units; u += kPlanThreads) s_cnt[u] = plan[L.cnt + u];
-  if (seq_lds)
-    for (int sq = tid; sq < a.batch; sq += kPlanThreads) {
-      live_rows(a.cu_q, sq, a.total_q, a.max_q_len, &s_seq[sq][0], &s_seq[sq][1]);
-      s_seq[sq][2] = clampi(a.kv_len[sq], 0, a.kv_cap);
+  // The header's length hash: the wrapping sum of every sequence's hash.
+  __shared__ unsigned s_hash;
+  if (tid == 0) s_hash = 0u;
+  __syncthreads();
+  unsigned my_hash = 0u;
+  for (int sq = tid; sq < a.batch; sq += kPlanThreads) {
+    int q0, ql;
+    live_rows(a.cu_q, sq, a.total_q, a.max_q_len, &q0, &ql);
+    const int kvl = clampi(a.kv_len[sq], 0, a.kv_cap);
+    my_hash += seq_len_hash(sq, q0, ql, kvl);
+    if (seq_lds) {
+      s_seq[sq][0] = q0;
+      s_seq[sq][1] = ql;
+      s_seq[sq][2] = kvl;
     }
+  }
+  atomicAdd(&s_hash, my_hash);
   __syncthreads();
   auto cnt_of = [&](int u) { return in_lds ? s_cnt[u] : plan[L.cnt + u]; };
   // Writes item `idx` (unit u, kv head g, ordinals [ob, oe), partial slot ps) with the
@@ -672,6 +684,14 @@ __device__ void plan_step(const PlanArgs& a) {
     plan[5] = a.tile_k;
     plan[6] = a.nqt;
     plan[7] = a.nkt;
+    plan[kHdrMagic] = kPlanMagic;
+    plan[kHdrBatch] = a.batch;
+    plan[kHdrHkv] = a.num_kv_heads;
+    plan[kHdrLenHash] = (int)s_hash;
+    plan[kHdrWindow] = a.window;
+    plan[kHdrModeB] = a.mode_b;
+    plan[kHdrTotalQ] = a.total_q;
+    plan[kHdrKvCap] = a.kv_cap;
   }
 }
 

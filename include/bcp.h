@@ -189,9 +189,10 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
                             hipStream_t stream);
 
 /*
- * kv_commit_block -- write finished rows into their cache pages ("KV Cache", step 3: after
- * a block is fully unmasked its keys and values are committed; "Fewer, smaller forwards",
- * Advancement 11: arena entries carry their position tag, here the block id).
+ * kv_commit_block -- write finished rows into their cache pages ("KV Cache", step 3: a
+ * block's keys and values are written to the cache by a separate pass once the block is
+ * decided; "Fewer, smaller forwards", Advancement 11: arena entries carry their position
+ * tag, here the block id).
  * For sequence s and r < cu_src[s+1]-cu_src[s]: source row
  *   row = src_row ? src_row[cu_src[s]+r] : cu_src[s]+r
  * is copied bit for bit from k_src/v_src [n_src, Hkv, d] to logical row dst_start[s]+r of

@@ -21,9 +21,18 @@ from workloads.device import DeviceCase
 pytestmark = pytest.mark.gpu
 
 
-def canvas_case(seed, batch=3, prompt=40, canvas=24, n_canvas=3, G=4, Hkv=2, d=128, P=16, dtype="bf16"):
+def canvas_case(seed, batch=3, prompt=40, canvas=24, n_canvas=3, G=4, Hkv=2, d=128, P=16, dtype="bf16",
+                shuffle=False):
+    """shuffle: the rows of each sequence in promotion order -- committed rows in random
+    slot order and live rows interleaved across canvases, each with its id and position."""
     rng = np.random.default_rng(seed)
     ql, kl, qb, kb, live_pos, com_pos = multi_canvas_structure(rng, batch, prompt, canvas, n_canvas)
+    if shuffle:
+        for s in range(batch):
+            p = rng.permutation(len(qb[s]))
+            qb[s], live_pos[s] = [qb[s][i] for i in p], [live_pos[s][i] for i in p]
+            p = rng.permutation(len(kb[s]))
+            kb[s], com_pos[s] = [kb[s][i] for i in p], [com_pos[s][i] for i in p]
     case = make_case(seed, dtype=dtype, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=d, block_size=1,
                      page_size=P, q_lens=ql, kv_lens=kl, q_blk_seqs=qb, kv_blk_seqs=kb,
                      qkv_std=1 / np.sqrt(d), rng=rng)
@@ -62,7 +71,13 @@ SMALL = [
     dict(seed=105, W=200, batch=4, prompt=300, canvas=64, n_canvas=4),       # wider than some sequences
     dict(seed=106, W=20, G=8, d=128, P=3),
     dict(seed=107, W=25, dtype="f32"),
-    dict(seed=108, W=12, G=16, Hkv=1, d=64, prompt=20, canvas=8, n_canvas=2, P=16),   # narrow q-tiles
+    # narrow q-tiles (at most 64 packed rows per sequence and kv head): the narrow kernel
+    dict(seed=108, W=12, G=4, Hkv=2, d=128, prompt=30, canvas=8, n_canvas=2, P=16, narrow=True),
+    dict(seed=109, W=5, G=16, Hkv=1, d=64, prompt=20, canvas=2, n_canvas=2, P=8, narrow=True),
+    # promotion order
+    dict(seed=110, W=30, shuffle=True),
+    dict(seed=115, W=200, batch=4, prompt=300, canvas=64, n_canvas=4, P=8, shuffle=True),
+    dict(seed=116, W=9, G=4, Hkv=2, d=128, prompt=40, canvas=8, n_canvas=2, P=16, narrow=True, shuffle=True),
 ]
 
 
@@ -70,8 +85,12 @@ SMALL = [
 def test_mode_B_window_small(spec):
     spec = dict(spec)
     W = spec.pop("W")
+    narrow = spec.pop("narrow", False)
     case, (q_pos, kv_pos) = canvas_case(**spec)
     say(f"mode-B window {W} case {spec}: q_lens {case.q_lens.tolist()} kv_lens {case.kv_len.tolist()}")
+    G = case.num_q_heads // case.num_kv_heads
+    meta = bcp.StepMeta(**DeviceCase(case).meta_kwargs())
+    assert (bcp.num_q_tiles(meta) == -(-case.max_q_len // (64 // G))) == narrow
     O_ref, L_ref = oracle_attention(case, window=W, q_pos=q_pos, kv_pos=kv_pos)
     out, lse, _ = run(case, q_pos, kv_pos, W)
     assert_close(out, O_ref, case.dtype, lse, L_ref, what=f"mode B window {W}")

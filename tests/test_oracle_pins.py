@@ -641,3 +641,67 @@ def test_commit_copies_position_tags():
     for r, (page, slot) in enumerate(g["slots"]):
         assert kvp[page * P + slot] == 40 + r
     assert np.count_nonzero(kvp >= 0) == 3
+
+
+# ------------------------------------------------ row chunks and row sampling --------
+# The oracle works through a sequence's live rows 512 at a time and can compute a chosen
+# subset of rows. Both paths are pinned here against SDPA on inputs long enough to cross
+# several chunk boundaries.
+
+def test_rows_beyond_one_chunk_equal_sdpa_token_causal():
+    """1100 token-causal rows (D=1, empty cache) -- three chunks of 512 -- against SDPA."""
+    rng = np.random.default_rng(71)
+    c, _ = contiguous_case(rng, q_len=1100, kv_len=0, Hq=4, Hkv=2, d=16, D=1, P=16)
+    O, L = run(c)
+    ref = sdpa64(c["q"], expand_gqa(c["k_new"], 2), expand_gqa(c["v_new"], 2), causal=True)
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+    # LSE of the first row (it sees only itself) is its own scaled score.
+    q0, k0 = c["q"][0].astype(np.float64), expand_gqa(c["k_new"], 2)[0].astype(np.float64)
+    np.testing.assert_allclose(L[0], (q0 * k0).sum(-1) / 4.0, rtol=0, atol=1e-12)
+
+
+def block_causal_mask(q_len, kv_len, D):
+    """Visibility written out per pair: cached keys always, live key j iff j // D <= i // D."""
+    m = np.zeros((q_len, kv_len + q_len), dtype=bool)
+    for i in range(q_len):
+        m[i, :kv_len] = True
+        for j in range(q_len):
+            m[i, kv_len + j] = (j // D) <= (i // D)
+    return m
+
+
+def test_rows_beyond_one_chunk_equal_sdpa_block_causal_over_cache():
+    """1030 live rows in blocks of 37 over a cache of 50 rows: the block edges fall at
+    different offsets in each 512-row chunk; SDPA with the mask written out pair by pair."""
+    rng = np.random.default_rng(72)
+    q_len, kv_len, D = 1030, 50, 37
+    c, (Kc, Vc) = contiguous_case(rng, q_len=q_len, kv_len=kv_len, Hq=2, Hkv=1, d=8, D=D, P=16)
+    O, _ = run(c)
+    K = expand_gqa(np.concatenate([Kc, c["k_new"]]), 2)
+    V = expand_gqa(np.concatenate([Vc, c["v_new"]]), 2)
+    ref = sdpa64(c["q"], K, V, mask=block_causal_mask(q_len, kv_len, D))
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+
+
+def test_sampled_rows_equal_sdpa_and_the_full_call():
+    """rows= computes exactly the chosen rows: against SDPA directly, and against the same
+    rows of the full call (rows on both sides of each chunk edge, out of order, repeated)."""
+    rng = np.random.default_rng(73)
+    q_len, kv_len, D = 1100, 70, 64
+    c, (Kc, Vc) = contiguous_case(rng, q_len=q_len, kv_len=kv_len, Hq=4, Hkv=1, d=16, D=D, P=8)
+    rows = np.array([1099, 0, 511, 512, 513, 700, 1023, 1024, 5, 512])
+    Os, Ls = oracle.attention_rows(c["q"], c["k_new"], c["v_new"], c["k_cache"], c["v_cache"], c["cu_q"],
+                                   c["kv_len"], c["page_table"], c["page_size"], c["num_pages"], 0,
+                                   rows=rows, block_size=D)
+    K = expand_gqa(np.concatenate([Kc, c["k_new"]]), 4)
+    V = expand_gqa(np.concatenate([Vc, c["v_new"]]), 4)
+    ref = sdpa64(c["q"], K, V, mask=block_causal_mask(q_len, kv_len, D))
+    np.testing.assert_allclose(Os, ref[rows], rtol=0, atol=1e-12)
+    O, L = run(c)
+    np.testing.assert_allclose(Os, O[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Ls, L[rows], rtol=0, atol=1e-12)
+    # Through the batch wrapper: the sampled rows are filled, every other row stays NaN.
+    Ob, _ = run(c, rows={0: rows})
+    np.testing.assert_allclose(Ob[rows], ref[rows], rtol=0, atol=1e-12)
+    others = np.setdiff1d(np.arange(q_len), rows)
+    assert np.isnan(Ob[others]).all()
