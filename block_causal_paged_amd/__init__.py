@@ -8,6 +8,7 @@ fallback: if the library is not built, every call raises.
 Entry points (same names as the C ABI):
   build_tile_mask(meta, tile_class=None, phys_page=None, plan=None)
   attn_block_causal_paged(meta, q, k_new, v_new, k_cache, v_cache, out, plan=None, ...)
+  attn_block_causal_paged_noalloc(meta, q, k_new, v_new, k_cache, v_cache, out, plan=None, ...)
   kv_commit_block(meta, k_src, v_src, cu_src, dst_start, k_cache, v_cache, total_commit, ...)
   graph_begin(stream), graph_end(stream) -> Graph, Graph.launch(stream), Graph.close()
     (bcp_graph_begin / _end / _launch / _destroy: capture a step's calls and replay them)
@@ -28,7 +29,8 @@ STATUS_NAMES = {0: "BCP_OK", 1: "BCP_E_ARG", 2: "BCP_E_UNSUPPORTED", 3: "BCP_E_R
 
 # Every function include/bcp.h declares.
 EXPORTED = ["bcp_num_q_tiles", "bcp_num_k_tiles", "bcp_plan_size", "build_tile_mask",
-            "attn_block_causal_paged_workspace_size", "attn_block_causal_paged", "kv_commit_block",
+            "attn_block_causal_paged_workspace_size", "attn_block_causal_paged",
+            "attn_block_causal_paged_noalloc", "kv_commit_block",
             "bcp_last_error", "bcp_abi_version", "bcp_graph_begin", "bcp_graph_end", "bcp_graph_launch",
             "bcp_graph_destroy"]
 
@@ -89,6 +91,8 @@ def lib():
         L.build_tile_mask.restype = ctypes.c_int
         L.attn_block_causal_paged.argtypes = [P, VP, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP, VP, SZ, VP, VP]
         L.attn_block_causal_paged.restype = ctypes.c_int
+        L.attn_block_causal_paged_noalloc.argtypes = [P, VP, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP, VP, VP]
+        L.attn_block_causal_paged_noalloc.restype = ctypes.c_int
         L.kv_commit_block.argtypes = [P, VP, VP, VP, VP, VP, VP, I32, I32, VP, VP, VP, VP]
         L.kv_commit_block.restype = ctypes.c_int
         L.bcp_graph_begin.argtypes, L.bcp_graph_begin.restype = [VP], ctypes.c_int
@@ -178,6 +182,18 @@ def attn_block_causal_paged(meta, q, k_new, v_new, k_cache, v_cache, out, plan=N
     _check(lib().attn_block_causal_paged(meta.ref, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                          _ptr(v_cache), _ptr(plan), float(scale), _ptr(out), _ptr(lse),
                                          _ptr(workspace), wbytes, _ptr(stats), _stream(stream, q)))
+
+
+NOALLOC_SCRATCH_BYTES = 76 << 20    # BCP_NOALLOC_SCRATCH_BYTES
+
+
+def attn_block_causal_paged_noalloc(meta, q, k_new, v_new, k_cache, v_cache, out, plan=None, scale=0.0,
+                                    lse=None, stats=None, stream=None):
+    """The allocation-free attention call: no workspace; the library's static per-GPU scratch
+    holds the split partials (and the plan when `plan` is None)."""
+    _check(lib().attn_block_causal_paged_noalloc(meta.ref, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                                 _ptr(v_cache), _ptr(plan), float(scale), _ptr(out), _ptr(lse),
+                                                 _ptr(stats), _stream(stream, q)))
 
 
 def kv_commit_block(meta, k_src, v_src, cu_src, dst_start, k_cache, v_cache, total_commit,

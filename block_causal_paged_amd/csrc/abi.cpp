@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 #include <unordered_set>
@@ -14,6 +15,13 @@
 #include "bcp_internal.h"
 
 using namespace bcp;
+
+// Scratch of the allocation-free attention entry point: the split-KV partial results and,
+// when the caller passes no plan, the plan. The runtime places one copy of the array in the
+// memory of every GPU that runs the library's code, for the life of the process. In host
+// code `scratch` names a host-side stand-in, not device memory: host code reaches a GPU's
+// copy only through the address hipGetSymbolAddress returns with that GPU current.
+static __device__ __align__(256) unsigned char scratch[BCP_NOALLOC_SCRATCH_BYTES];
 
 // A captured step: the HIP graph and its executable instance.
 struct bcp_graph {
@@ -231,6 +239,31 @@ int device_cus() {
   return n;
 }
 
+// Device address of the current GPU's copy of `scratch`, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(BCP_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(BCP_E_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BCP_OK;
+}
+
 size_t plan_bytes_for(const bcp_meta* m, const Geo& g) {
   return (size_t)plan_layout(m->batch, g.nqt, g.nkt, m->num_kv_heads).words * sizeof(int32_t);
 }
@@ -399,10 +432,15 @@ size_t attn_block_causal_paged_workspace_size(const bcp_meta* m) {
   return part + plan_bytes_for(m, g) + 256;
 }
 
-int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new, const void* v_new,
-                            const void* k_cache, const void* v_cache, const void* plan, float scale,
-                            void* out, float* lse, void* workspace, size_t workspace_bytes,
-                            uint64_t* stats, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The attention call. With noalloc the workspace is this GPU's copy of `scratch` (the
+// workspace arguments are ignored), found after every host-side check has passed.
+int attn_impl(const bcp_meta* m, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+              const void* v_cache, const void* plan, float scale, void* out, float* lse, void* workspace,
+              size_t workspace_bytes, uint64_t* stats, hipStream_t stream, bool noalloc) {
   Geo g;
   int rc = check_meta(m, &g);
   if (rc) return rc;
@@ -418,13 +456,25 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
   if (!std::isfinite(scale)) return fail(BCP_E_ARG, "scale is not finite");
   const size_t part = partial_bytes_for(m, g);
   const size_t need = part + (plan ? 0 : plan_bytes_for(m, g) + 256);
-  if (workspace_bytes < need || (need && !workspace))
-    return fail(BCP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  if (workspace && !aligned(workspace, 16)) return fail(BCP_E_ARG, "workspace must be 16-byte aligned");
+  if (noalloc) {
+    if (need > (size_t)BCP_NOALLOC_SCRATCH_BYTES)
+      return fail(BCP_E_WORKSPACE,
+                  "the allocation-free call needs %zu bytes of scratch (%s), more than its %zu; pass a plan "
+                  "from build_tile_mask or use attn_block_causal_paged with a workspace",
+                  need, plan ? "split-KV partials" : "split-KV partials and the plan", (size_t)BCP_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (workspace_bytes < need || (need && !workspace))
+      return fail(BCP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (workspace && !aligned(workspace, 16)) return fail(BCP_E_ARG, "workspace must be 16-byte aligned");
+  }
   if (m->flags & BCP_F_CHECK) {
     uint32_t len_hash = 0;
     if ((rc = validate_metadata(m, stream, &len_hash))) return rc;
     if (plan && (rc = validate_plan(m, g, plan, len_hash, stream))) return rc;
+  }
+  if (noalloc && need) {
+    if ((rc = scratch_address(&workspace))) return rc;
+    workspace_bytes = BCP_NOALLOC_SCRATCH_BYTES;
   }
   g_err.clear();
   if (m->total_q == 0 || g.nqt == 0) return BCP_OK;
@@ -494,6 +544,24 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
     if (e != hipSuccess) return hip_fail(e, "launch combine");
   }
   return BCP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new, const void* v_new,
+                            const void* k_cache, const void* v_cache, const void* plan, float scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            uint64_t* stats, hipStream_t stream) {
+  return attn_impl(m, q, k_new, v_new, k_cache, v_cache, plan, scale, out, lse, workspace, workspace_bytes,
+                   stats, stream, false);
+}
+
+int attn_block_causal_paged_noalloc(const bcp_meta* m, const void* q, const void* k_new, const void* v_new,
+                                    const void* k_cache, const void* v_cache, const void* plan, float scale,
+                                    void* out, float* lse, uint64_t* stats, hipStream_t stream) {
+  return attn_impl(m, q, k_new, v_new, k_cache, v_cache, plan, scale, out, lse, nullptr, 0, stats, stream, true);
 }
 
 int kv_commit_block(const bcp_meta* m, const void* k_src, const void* v_src, const int32_t* cu_src,

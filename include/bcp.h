@@ -189,6 +189,27 @@ int attn_block_causal_paged(const bcp_meta* m, const void* q, const void* k_new,
                             hipStream_t stream);
 
 /*
+ * attn_block_causal_paged_noalloc -- attn_block_causal_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that forbid hipMalloc,
+ * harnesses that forbid allocation): the same computation and kernels, bit for bit, but no
+ * workspace argument. Its split-KV partial results (and the plan, when plan is NULL) live in
+ * a static device array of BCP_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * GPU it runs on until the process ends; the call itself allocates nothing. Every call on a
+ * GPU shares that GPU's array, so calls on one GPU that overlap in time (on different
+ * streams, say) race: issue them on one stream, or use attn_block_causal_paged with a
+ * workspace each. The array keeps whatever the last call left; nothing in it needs to start
+ * at zero. The first call on a device looks up that device's copy (hipGetSymbolAddress).
+ * Errors: as attn_block_causal_paged, and BCP_E_WORKSPACE when the step needs more scratch
+ * than the array holds (64.5 MiB of partial results at head_dim 128, plus the plan when it
+ * is NULL; a plan from build_tile_mask keeps any step within the limit).
+ */
+#define BCP_NOALLOC_SCRATCH_BYTES (76u << 20)
+int attn_block_causal_paged_noalloc(const bcp_meta* m, const void* q, const void* k_new,
+                                    const void* v_new, const void* k_cache, const void* v_cache,
+                                    const void* plan, float scale, void* out, float* lse,
+                                    uint64_t* stats, hipStream_t stream);
+
+/*
  * kv_commit_block -- write finished rows into their cache pages ("KV Cache", step 3: a
  * block's keys and values are written to the cache by a separate pass once the block is
  * decided; "Fewer, smaller forwards", Advancement 11: arena entries carry their position

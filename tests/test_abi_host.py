@@ -154,3 +154,20 @@ def test_graph_entry_points_reject_null_handles():
 def test_error_message_is_thread_local_and_specific():
     attn(meta(head_dim=96))
     assert b"head_dim 96" in bcp.lib().bcp_last_error()
+
+
+def test_noalloc_rejects_a_step_beyond_its_scratch_before_any_hip_call():
+    """The allocation-free call refuses a step whose scratch need (partials plus, with no plan,
+    the plan) exceeds its static array, with BCP_E_WORKSPACE, before touching a device."""
+    m = meta(max_q_len=100000, total_q=512)     # the plan's per-q-tile lists grow with the bound
+    L = bcp.lib()
+    need = L.bcp_plan_size(ctypes.byref(m))
+    assert need > bcp.NOALLOC_SCRATCH_BYTES
+    rc = L.attn_block_causal_paged_noalloc(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.0, FAKE, None,
+                                           None, None)
+    assert rc == bcp.BCP_E_WORKSPACE
+    assert b"allocation-free" in L.bcp_last_error()
+    # Host-argument errors come first, as for the ordinary call.
+    rc = L.attn_block_causal_paged_noalloc(ctypes.byref(meta(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                           0.0, FAKE, None, None, None)
+    assert rc == bcp.BCP_E_UNSUPPORTED
