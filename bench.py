@@ -86,17 +86,22 @@ def summarize_traffic(args):
         copies = [v for k, v in d if "MulFunctor" in k]
         calib = float(np.median(copies[-5:])) * 1024.0
         factor = CALIB_BYTES / calib
-        calls, cur = [], None
+        calls, commits, cur = [], [], None
         for k, v in d:
             if "attn_bf16_kernel" in k or "attn_bf16_narrow_kernel" in k or "attn_f32_kernel" in k:
                 cur = [v]
                 calls.append(cur)
             elif "combine_kernel" in k and cur is not None:
                 cur.append(v)
+            elif "commit_kernel" in k:
+                commits.append(v)
         cold = calls[args.warmup:args.warmup + args.steps]
+        cold_commits = commits[args.warmup:args.warmup + args.steps]
         out[name] = {"calib_counter_bytes": calib, "factor": factor,
                      "bytes_per_call": float(np.median([sum(c) for c in cold])) * 1024.0 * factor,
                      "attn_kernel_bytes": float(np.median([c[0] for c in cold])) * 1024.0 * factor,
+                     "commit_kernel_bytes": (float(np.median(cold_commits)) * 1024.0 * factor
+                                             if cold_commits else None),
                      "cold_calls": len(cold)}
     rec = {"config": args.config, "kernel_hash": kernel_hash(),
            "hbm_bytes_per_call": out["fetch"]["bytes_per_call"] + out["write"]["bytes_per_call"],
@@ -124,6 +129,10 @@ def summarize_traffic(args):
                     f"{o['bytes_per_call']:.4g} | {o['attn_kernel_bytes']:.4g} |\n")
         f.write(f"\nHBM bytes per call (fetch + write): {rec['hbm_bytes_per_call']:.4g}; kernel code hash (comments stripped) "
                 f"{rec['kernel_hash']} (bench.py reports it as roofline.traffic only while the hash matches).\n")
+        if out["fetch"]["commit_kernel_bytes"] is not None:
+            cf, cw = out["fetch"]["commit_kernel_bytes"], out["write"]["commit_kernel_bytes"]
+            f.write(f"\nThe step's kv_commit_block (commit_kernel), same runs: {cf:.4g} bytes fetched and {cw:.4g} "
+                    f"written per call ({cf + cw:.4g} in all).\n")
     print(json.dumps(rec))
 
 
