@@ -328,6 +328,23 @@ int run_classify_and_plan(const bcp_meta* m, const Geo& g, uint8_t* tile_class, 
   p.kv_cap = m->max_pages_per_seq * m->page_size;
   p.window = m->window;
   p.mode_b = g.mode_b ? 1 : 0;
+  // A small mode-A step without a window is classified by the planner itself: one launch.
+  const int64_t elems = (int64_t)m->batch * g.nqt * g.nkt + (phys_page ? (int64_t)m->batch * g.nct * a.phys_per_tile : 0);
+  if (plan && !g.mode_b && m->window == 0 && m->batch <= 1024 && elems <= kFusedPlanElems) {
+    p.fused = 1;
+    p.nct = g.nct;
+    p.block_size = m->block_size;
+    p.page_size = m->page_size;
+    p.num_pages = m->num_pages;
+    p.max_pages = m->max_pages_per_seq;
+    p.phys_per_tile = a.phys_per_tile;
+    p.tile_class = tile_class;
+    p.phys_page = phys_page;
+    p.page_table = m->page_table;
+    hipError_t e = launch_planner(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "launch planner");
+    return BCP_OK;
+  }
   hipError_t e = launch_classify(a, stream);
   if (e != hipSuccess) return hip_fail(e, "launch classify");
   if (plan) {

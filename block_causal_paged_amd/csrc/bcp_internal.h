@@ -135,7 +135,17 @@ struct PlanArgs {
   int batch, nqt, nkt, num_kv_heads, tile_q, tile_k;
   int total_q, max_q_len, kv_cap;   // kv_cap = max_pages_per_seq * page_size
   int window, mode_b;               // recorded in the header (with total_q and kv_cap)
+  // Small mode-A steps without a window: the planner classifies the tiles itself (closed form)
+  // and writes the tile lists, and the classes and physical pages when asked, so that
+  // build_tile_mask is one launch.
+  int fused;
+  int nct, block_size, page_size, num_pages, max_pages, phys_per_tile;
+  uint8_t* tile_class;              // may be null
+  int32_t* phys_page;               // may be null
+  const int32_t* page_table;
 };
+// Largest class and page-entry count of a step the planner classifies itself.
+constexpr int kFusedPlanElems = 4096;
 
 struct AttnArgs {
   const void* q;

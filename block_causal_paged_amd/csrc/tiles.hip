@@ -423,7 +423,7 @@ __device__ void plan_step(const PlanArgs& a) {
   __shared__ int s_seq[kPlanLdsSeqs][3];
   const bool in_lds = units <= kPlanLdsUnits;
   const bool seq_lds = a.batch <= kPlanLdsSeqs;
-  if (in_lds)
+  if (in_lds && !a.fused)
     for (int u = tid; u < units; u += kPlanThreads) s_cnt[u] = plan[L.cnt + u];
   // The header's length hash: the wrapping sum of every sequence's hash.
   __shared__ unsigned s_hash;
@@ -443,6 +443,69 @@ __device__ void plan_step(const PlanArgs& a) {
   }
   atomicAdd(&s_hash, my_hash);
   __syncthreads();
+  if (a.fused) {
+    // Mode A without a window (the host picks this only for such steps of at most
+    // kFusedPlanElems classes and page entries, with the sequences in LDS). A committed key is
+    // seen by every live row, so cached tile t is FULL when all tile_k of its keys exist,
+    // PARTIAL when some do, SKIP when none; live tile j (keys lo..hi) is SKIP when it has no
+    // key or its first key's block lo/D lies after the q-tile's last row's block, FULL when
+    // its last key's block is at most the q-tile's first row's block and it has all tile_k
+    // keys, PARTIAL otherwise. In both regions the non-skipped tiles are a prefix, so a
+    // tile's place in its unit's list follows from the counts without a scan.
+    const int tq = a.tile_q, tk = a.tile_k, D = a.block_size, nlt = a.nkt - a.nct;
+    auto unit_geo = [&](int u, int* ql, int* kvl, int* i0, int* i1, int* nc, int* nl) {
+      const int sq = u / a.nqt, r = u - sq * a.nqt;
+      *ql = s_seq[sq][1];
+      *kvl = s_seq[sq][2];
+      *i0 = r * tq;
+      *i1 = min(*i0 + tq, *ql);
+      if (*i1 <= *i0) {
+        *nc = *nl = 0;
+        return;
+      }
+      *nc = min((*kvl + tk - 1) / tk, a.nct);
+      const int64_t qmax = (*i1 - 1) / D;
+      const int64_t reach = (qmax * D + D - 1) / tk + 1;   // live tiles whose first key's block <= qmax
+      *nl = (int)min<int64_t>(min((*ql + tk - 1) / tk, nlt), reach);
+    };
+    for (int u = tid; u < units; u += kPlanThreads) {
+      int ql, kvl, i0, i1, nc, nl;
+      unit_geo(u, &ql, &kvl, &i0, &i1, &nc, &nl);
+      plan[L.cnt + u] = nc + nl;
+      if (in_lds) s_cnt[u] = nc + nl;
+    }
+    for (int idx = tid; idx < units * a.nkt; idx += kPlanThreads) {
+      const int u = idx / a.nkt, t = idx - u * a.nkt;
+      int ql, kvl, i0, i1, nc, nl;
+      unit_geo(u, &ql, &kvl, &i0, &i1, &nc, &nl);
+      int cls = BCP_TILE_SKIP, at = -1;
+      if (t < a.nct) {
+        if (t < nc) {
+          cls = kvl - t * tk >= tk ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
+          at = t;
+        }
+      } else if (t - a.nct < nl) {
+        const int lo = (t - a.nct) * tk, nvalid = min(ql - lo, tk);
+        const bool full = (lo + nvalid - 1) / D <= i0 / D && nvalid == tk;
+        cls = full ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
+        at = nc + (t - a.nct);
+      }
+      if (a.tile_class) a.tile_class[idx] = (uint8_t)cls;
+      if (at >= 0) plan[L.list + (int64_t)u * a.nkt + at] = (t << 1) | (cls == BCP_TILE_PARTIAL ? 1 : 0);
+    }
+    if (a.phys_page) {
+      const int per_seq = a.nct * a.phys_per_tile;
+      for (int idx = tid; idx < a.batch * per_seq; idx += kPlanThreads) {
+        const int sq = idx / per_seq, rem = idx - sq * per_seq;
+        const int t = rem / a.phys_per_tile, k = rem - t * a.phys_per_tile;
+        const int row = t * tk + k * a.page_size;
+        int p = -1;
+        if (row < s_seq[sq][2]) p = translate_page(a.page_table, sq, row, a.page_size, a.max_pages, a.num_pages);
+        a.phys_page[idx] = p;
+      }
+    }
+    __syncthreads();   // the counts (in the plan when they do not fit in LDS) are read below
+  }
   auto cnt_of = [&](int u) { return in_lds ? s_cnt[u] : plan[L.cnt + u]; };
   // Writes item `idx` (unit u, kv head g, ordinals [ob, oe), partial slot ps) with the
   // unit's live rows and committed length, which the attention kernel then reads with the
