@@ -440,8 +440,18 @@ __device__ __forceinline__ void run_rows(const AttnArgs& a, const Item& it, cons
 // the loads of tile x+3 (keys) or x+4 (values) start in H(2x+2) or later: three key
 // stages and four value stages suffice.
 // BAND_B: mode B with a sliding window (keys' positions staged beside their block ids).
-template <int HD, bool BAND_B>
+// LEAN: mode A without a window, live rows passed in (the decode and prefill shapes); the
+// other paths' state and branches drop out of the tile loop, which frees registers.
+__device__ __forceinline__ void make_lean(AttnArgs& a) {
+  a.mode_b = 0;
+  a.window = 0;
+  a.live_in_cache = 0;
+  a.q_blk = a.kv_blk = a.q_pos = a.kv_pos = nullptr;
+}
+
+template <int HD, bool BAND_B, bool LEAN>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
+  if constexpr (LEAN) make_lean(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16;       // MFMA steps over d for the scores
@@ -892,8 +902,9 @@ __device__ __forceinline__ void wait_vm_in(int n) {
   }
 }
 
-template <int HD, bool BAND_B>
+template <int HD, bool BAND_B, bool LEAN>
 __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a) {
+  if constexpr (LEAN) make_lean(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16, NDB = HD / 32;
@@ -1218,27 +1229,33 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
   const bool band_b = a.mode_b && a.window > 0;
-  if (head_dim == 128 && !band_b)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else if (!band_b)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<64, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  const bool lean = !a.mode_b && a.window == 0 && !a.live_in_cache;
+  const dim3 g(grid), b(kThreads);
+  if (head_dim == 128) {
+    if (lean) hipLaunchKernelGGL((attn_bf16_kernel<128, false, true>), g, b, 0, stream, a);
+    else if (band_b) hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, false, false>), g, b, 0, stream, a);
+  } else {
+    if (lean) hipLaunchKernelGGL((attn_bf16_kernel<64, false, true>), g, b, 0, stream, a);
+    else if (band_b) hipLaunchKernelGGL((attn_bf16_kernel<64, true, false>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, false, false>), g, b, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16_narrow(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
   const bool band_b = a.mode_b && a.window > 0;
-  if (head_dim == 128 && !band_b)
-    hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false>), dim3(grid), dim3(kNThreads), 0, stream, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, true>), dim3(grid), dim3(kNThreads), 0, stream, a);
-  else if (!band_b)
-    hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false>), dim3(grid), dim3(kNThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, true>), dim3(grid), dim3(kNThreads), 0, stream, a);
+  const bool lean = !a.mode_b && a.window == 0 && !a.live_in_cache;
+  const dim3 g(grid), b(kNThreads);
+  if (head_dim == 128) {
+    if (lean) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, true>), g, b, 0, stream, a);
+    else if (band_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, true, false>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, false>), g, b, 0, stream, a);
+  } else {
+    if (lean) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, true>), g, b, 0, stream, a);
+    else if (band_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, true, false>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, false>), g, b, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
