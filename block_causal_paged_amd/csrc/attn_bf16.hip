@@ -173,6 +173,20 @@ __device__ __forceinline__ int tile_valid(const AttnArgs& a, const Item& it, int
   return vt < a.nct ? clampi(it.kvl - vt * kTileK, 0, kTileK) : clampi(it.q_len - (vt - a.nct) * kTileK, 0, kTileK);
 }
 
+// Plan entry of a unit's o-th non-skipped key tile in mode A without a window, from the
+// unit's lengths alone (the same entry the planner writes): the non-skipped tiles are the
+// first nc cached tiles, then the first live tiles; a cached tile is partial only where the
+// committed rows end inside it, a live tile unless all its keys exist and lie in blocks no
+// later than the q-tile's first row's (qmin).
+__device__ __forceinline__ int mode_a_entry(const AttnArgs& a, const Item& it, int nc, int qmin, int o) {
+  if (o < nc) return (o << 1) | (it.kvl - o * kTileK < kTileK ? 1 : 0);
+  const int lo = (o - nc) * kTileK, nv = min(it.q_len - lo, kTileK);
+  return ((a.nct + o - nc) << 1) | (nv == kTileK && (lo + nv - 1) / a.block_size <= qmin ? 0 : 1);
+}
+__device__ __forceinline__ int mode_a_cached(const AttnArgs& a, const Item& it) {
+  return min((it.kvl + kTileK - 1) / kTileK, a.nct);
+}
+
 // Staging state of one key tile for one wave: the plan entry and the memory row of the
 // wave's first key row (rows of the kv cache for a cached tile, and for a live tile when
 // the live rows are read from the pool; else rows of the new keys), -1 when the wave's
@@ -537,10 +551,20 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     int tq = tid;
     asm volatile("" : "+v"(tq));   // slot math stays here, not hoisted out of the item loop
     auto win_load_entries = [&](int wb, int nt) {
+      if constexpr (LEAN) {
+        // Mode A without a window: the entries follow from the unit's lengths, with no load.
+        const int nc = mode_a_cached(a, it), qmin = i0 / a.block_size;
 #pragma unroll
-      for (int k = 0; k < kWinPerThread; ++k) {
-        const int i = tq + k * kThreads;
-        we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
+        for (int k = 0; k < kWinPerThread; ++k) {
+          const int i = tq + k * kThreads;
+          we[k] = i < nt * kWaves ? mode_a_entry(a, it, nc, qmin, wb + i / kWaves) : 0;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kWinPerThread; ++k) {
+          const int i = tq + k * kThreads;
+          we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
+        }
       }
     };
     auto win_load_rows = [&](int nt) { run_rows<kWinPerThread>(a, it, pt, we, tq, kThreads, nt, wr); };
@@ -979,10 +1003,12 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
     // every 8-row run of every tile (-1: general path; <= -2: a live run crossing a page).
     auto win_stage = [&](int wb, int nt) {
       int we[kNWinPerThread], wr[kNWinPerThread];
+      const int nc = mode_a_cached(a, it), qmin = i0 / a.block_size;   // (lean instance)
 #pragma unroll
       for (int k = 0; k < kNWinPerThread; ++k) {
         const int i = tid + k * kNThreads;
-        we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
+        if constexpr (LEAN) we[k] = i < nt * kWaves ? mode_a_entry(a, it, nc, qmin, wb + i / kWaves) : 0;
+        else we[k] = i < nt * kWaves ? list[wb + i / kWaves] : 0;
       }
       run_rows<kNWinPerThread>(a, it, pt, we, tid, kNThreads, nt, wr);
       __syncthreads();   // earlier readers of the window (previous window or item) are done
