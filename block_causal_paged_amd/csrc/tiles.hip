@@ -452,56 +452,83 @@ __device__ void plan_step(const PlanArgs& a) {
     // its last key's block is at most the q-tile's first row's block and it has all tile_k
     // keys, PARTIAL otherwise. In both regions the non-skipped tiles are a prefix, so a
     // tile's place in its unit's list follows from the counts without a scan.
+    // Per unit, four counts: its non-skipped cached tiles nc, the first nfc of them FULL (all
+    // tile_k keys committed), and its non-skipped live tiles nl, the first nfl of them FULL.
+    // Live tile j is non-skipped when its first key j*tile_k lies in a block no later than
+    // the q-tile's last row's block qmax, i.e. j*tile_k < (qmax+1)*D; it is FULL when it has
+    // tile_k keys all in blocks no later than the first row's block qmin, i.e.
+    // (j+1)*tile_k <= min(q_len, (qmin+1)*D). A fused step has at most kFusedPlanElems
+    // tiles, so each pair of counts packs into one word of the (not yet used) scan arrays.
     const int tq = a.tile_q, tk = a.tile_k, D = a.block_size, nlt = a.nkt - a.nct;
-    auto unit_geo = [&](int u, int* ql, int* kvl, int* i0, int* i1, int* nc, int* nl) {
-      const int sq = u / a.nqt, r = u - sq * a.nqt;
-      *ql = s_seq[sq][1];
-      *kvl = s_seq[sq][2];
-      *i0 = r * tq;
-      *i1 = min(*i0 + tq, *ql);
-      if (*i1 <= *i0) {
-        *nc = *nl = 0;
-        return;
-      }
-      *nc = min((*kvl + tk - 1) / tk, a.nct);
-      const int64_t qmax = (*i1 - 1) / D;
-      const int64_t reach = (qmax * D + D - 1) / tk + 1;   // live tiles whose first key's block <= qmax
-      *nl = (int)min<int64_t>(min((*ql + tk - 1) / tk, nlt), reach);
-    };
     for (int u = tid; u < units; u += kPlanThreads) {
-      int ql, kvl, i0, i1, nc, nl;
-      unit_geo(u, &ql, &kvl, &i0, &i1, &nc, &nl);
-      plan[L.cnt + u] = nc + nl;
-      if (in_lds) s_cnt[u] = nc + nl;
-    }
-    for (int idx = tid; idx < units * a.nkt; idx += kPlanThreads) {
-      const int u = idx / a.nkt, t = idx - u * a.nkt;
-      int ql, kvl, i0, i1, nc, nl;
-      unit_geo(u, &ql, &kvl, &i0, &i1, &nc, &nl);
-      int cls = BCP_TILE_SKIP, at = -1;
-      if (t < a.nct) {
-        if (t < nc) {
-          cls = kvl - t * tk >= tk ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
-          at = t;
-        }
-      } else if (t - a.nct < nl) {
-        const int lo = (t - a.nct) * tk, nvalid = min(ql - lo, tk);
-        const bool full = (lo + nvalid - 1) / D <= i0 / D && nvalid == tk;
-        cls = full ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
-        at = nc + (t - a.nct);
+      const int sq = u / a.nqt, r = u - sq * a.nqt;
+      const int ql = s_seq[sq][1], kvl = s_seq[sq][2];
+      const int i0 = r * tq, i1 = min(i0 + tq, ql);
+      int nc = 0, nfc = 0, nl = 0, nfl = 0;
+      if (i1 > i0) {
+        nc = min((kvl + tk - 1) / tk, a.nct);
+        nfc = min(kvl / tk, a.nct);
+        const int64_t qmax = (i1 - 1) / D, qmin = i0 / D;
+        const int reach = (int)min<int64_t>((qmax + 1) * D, ql);   // keys a row of the q-tile may see
+        const int full = (int)min<int64_t>((qmin + 1) * D, ql);    // keys every row of it sees
+        nl = min((reach + tk - 1) / tk, nlt);
+        nfl = min(full / tk, nl);
       }
-      if (a.tile_class) a.tile_class[idx] = (uint8_t)cls;
-      if (at >= 0) plan[L.list + (int64_t)u * a.nkt + at] = (t << 1) | (cls == BCP_TILE_PARTIAL ? 1 : 0);
+      plan[L.cnt + u] = nc + nl;
+      s_cnt[u] = nc + nl;
+      s_upre[u] = nc | (nfc << 16);
+      s_nepre[u] = nl | (nfl << 16);
+    }
+    __syncthreads();
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      for (int u = wave; u < units; u += kPlanThreads / 64) {
+        const int cw = s_upre[u], lw = s_nepre[u];
+        const int nc = cw & 0xffff, nfc = cw >> 16, nl = lw & 0xffff, nfl = lw >> 16;
+        int* list = plan + L.list + (int64_t)u * a.nkt;
+        for (int t = lane; t < a.nkt; t += 64) {
+          const int j = t - a.nct;   // live tile ordinal (negative for cached tiles)
+          const bool on = j < 0 ? t < nc : j < nl;
+          const bool full = j < 0 ? t < nfc : j < nfl;
+          const int cls = !on ? BCP_TILE_SKIP : full ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
+          if (a.tile_class) a.tile_class[(int64_t)u * a.nkt + t] = (uint8_t)cls;
+          if (on) list[j < 0 ? t : nc + j] = (t << 1) | (full ? 0 : 1);
+        }
+      }
     }
     if (a.phys_page) {
-      const int per_seq = a.nct * a.phys_per_tile;
-      for (int idx = tid; idx < a.batch * per_seq; idx += kPlanThreads) {
-        const int sq = idx / per_seq, rem = idx - sq * per_seq;
-        const int t = rem / a.phys_per_tile, k = rem - t * a.phys_per_tile;
-        const int row = t * tk + k * a.page_size;
-        int p = -1;
-        if (row < s_seq[sq][2]) p = translate_page(a.page_table, sq, row, a.page_size, a.max_pages, a.num_pages);
-        a.phys_page[idx] = p;
+      // Entry (sq, t, k) is the page of row t*tile_k + k*page_size; when pages tile the key
+      // tiles exactly that row is e*page_size for the entry's ordinal e inside its sequence.
+      // The loads of a batch of entries are issued before any of their stores.
+      const int ppt = a.phys_per_tile, per_seq = a.nct * ppt, P = a.page_size;
+      const bool whole = tk % P == 0;
+      const int total = a.batch * per_seq;
+      constexpr int kB = 4;
+      for (int base = 0; base < total; base += kB * kPlanThreads) {
+        int pv[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = base + b * kPlanThreads + tid;
+          pv[b] = -1;
+          if (idx < total) {
+            const int sq = idx / per_seq, e = idx - sq * per_seq;
+            int row, lp;
+            if (whole) {
+              row = e * P;
+              lp = e;
+            } else {
+              const int t = e / ppt, k = e - t * ppt;
+              row = t * tk + k * P;
+              lp = row / P;
+            }
+            if (row < s_seq[sq][2] && lp < a.max_pages) pv[b] = a.page_table[(int64_t)sq * a.max_pages + lp];
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = base + b * kPlanThreads + tid;
+          if (idx < total) a.phys_page[idx] = pv[b] >= 0 && pv[b] < a.num_pages ? pv[b] : -1;
+        }
       }
     }
     __syncthreads();   // the counts (in the plan when they do not fit in LDS) are read below
@@ -564,9 +591,83 @@ __device__ void plan_step(const PlanArgs& a) {
 
   const unsigned W = (unsigned)total_tiles * (unsigned)hkv;
   const int pairs = units * hkv;
-  unsigned n_wg;
-  Int3 all;
-  if (pairs <= kPlanThreads) {
+  unsigned n_wg = 1;
+  Int3 all = {0, 0, 0};
+  // Items k = 0..n-1 of a pair of cnt visits cut into n near-equal chunks: chunk k covers
+  // ordinals [floor(k*cnt/n), floor((k+1)*cnt/n)), stepped without a division per item.
+  auto put_chunks = [&](int first, int u, int g, int cnt, int n, int slot0) {
+    const int q = n > 0 ? cnt / n : 0, rr = cnt - q * n;
+    int ob = 0, acc = 0;
+    for (int k = 0; k < n; ++k) {
+      int oe = ob + q;
+      acc += rr;
+      if (acc >= n) {
+        acc -= n;
+        ++oe;
+      }
+      put_item(first + k, u, g, ob, oe, slot0 >= 0 ? slot0 + k : -1, first + k);
+      wg_first[first + k] = first + k;
+      ob = oe;
+    }
+  };
+  // The chunk length search of the decode path below: among kCand candidate lengths
+  // lo + step*(j+1) (capped at hi) it keeps the smallest whose chunk count fits in kWGs as
+  // the new hi and the largest that does not as the new lo. count(j) is the chunk count at
+  // candidate j summed over all pairs.
+  constexpr int kCand = 8;
+  auto narrow = [&](int& lo, int& hi, int step, auto count) {
+    int new_lo = lo, new_hi = hi;
+#pragma unroll
+    for (int j = kCand - 1; j >= 0; --j) {
+      const int cj = min(lo + step * (j + 1), hi);
+      if (count(j) <= kWGs) new_hi = cj;   // the smallest fitting candidate wins
+      else if (new_lo == lo) new_lo = cj;  // the largest failing candidate
+    }
+    lo = new_lo;   // chunk counts fall as the length grows, so new_lo < new_hi
+    hi = new_hi;
+  };
+  if (pairs <= 64) {
+    // The decode path below with every pair on a lane of wave 0: its sums and its scan are
+    // wave operations, with no barrier (the other waves wait at the next one).
+    if (tid < 64) {
+      const int pr = tid;
+      const int u = pr < pairs ? pr % units : 0, g = pr < pairs ? pr / units : 0;
+      const int cnt = pr < pairs ? cnt_of(u) : 0;
+      const int cmax = wave_max_nonneg(cnt);
+      int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
+      if (cmax > c) {
+        int lo = c - 1, hi = cmax;
+        bool first = true;
+        while (hi - lo > 1) {
+          const int step = first ? 1 : (hi - lo + kCand) / (kCand + 1);
+          first = false;
+          int sums[kCand];
+#pragma unroll
+          for (int j = 0; j < kCand; ++j) {
+            const int cj = min(lo + step * (j + 1), hi);
+            sums[j] = wave_sum((cnt + cj - 1) / cj);
+          }
+          narrow(lo, hi, step, [&](int j) { return sums[j]; });
+        }
+        c = hi;
+      }
+      const int n = cnt > 0 ? (cnt + c - 1) / c : 0;
+      const bool split = n > 1;
+      const int in = wave_scan_incl(n), isp = wave_scan_incl(split ? n : 0), ip = wave_scan_incl(split ? 1 : 0);
+      all = Int3{__builtin_amdgcn_readlane(in, 63), __builtin_amdgcn_readlane(isp, 63),
+                 __builtin_amdgcn_readlane(ip, 63)};
+      const Int3 at = {in - n, isp - (split ? n : 0), ip - (split ? 1 : 0)};
+      put_chunks(at.x, u, g, cnt, n, split ? at.y : -1);
+      if (split) {
+        int* sp = plan + L.split + 4 * (int64_t)at.z;
+        sp[0] = u;
+        sp[1] = g;
+        sp[2] = at.y;
+        sp[3] = n;
+      }
+      n_wg = max(1, all.x);
+    }
+  } else if (pairs <= kPlanThreads) {
     // Few (unit, kv head) pairs (decode batches): cut each pair into ceil(cnt/c) near-equal
     // chunks, one range each, with the smallest chunk length c >= max(kMinChunk,
     // ceil(W/kWGs)) that keeps the chunk count within kWGs (the count only falls as c
@@ -579,7 +680,6 @@ __device__ void plan_step(const PlanArgs& a) {
     // first round tries the kCand lengths from the lower bound up, which settles the usual
     // case; later rounds spread the candidates over the remaining interval, which shrinks
     // to the gap between the last length that gives too many chunks and the next one.
-    constexpr int kCand = 8;
     __shared__ int cand_lds[kPlanThreads / 64][kCand];
     const int cmax = block_max_nonneg(cnt, (int*)scan_lds);
     int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
@@ -597,30 +697,20 @@ __device__ void plan_step(const PlanArgs& a) {
           if (lane == 0) cand_lds[wave][j] = nj;
         }
         __syncthreads();
-        int new_lo = lo, new_hi = hi;
-#pragma unroll
-        for (int j = kCand - 1; j >= 0; --j) {
+        narrow(lo, hi, step, [&](int j) {
           int tot = 0;
 #pragma unroll
           for (int w = 0; w < kPlanThreads / 64; ++w) tot += cand_lds[w][j];
-          const int cj = min(lo + step * (j + 1), hi);
-          if (tot <= kWGs) new_hi = cj;        // the smallest fitting candidate wins
-          else if (new_lo == lo) new_lo = cj;  // the largest failing candidate
-        }
+          return tot;
+        });
         __syncthreads();
-        lo = new_lo;   // chunk counts fall as the length grows, so new_lo < new_hi
-        hi = new_hi;
       }
       c = hi;
     }
     const int n = cnt > 0 ? (cnt + c - 1) / c : 0;
     const bool split = n > 1;
     const Int3 at = block_scan3_excl(Int3{n, split ? n : 0, split ? 1 : 0}, scan_lds, &all);
-    for (int k = 0; k < n; ++k) {
-      put_item(at.x + k, u, g, (int)(((long long)k * cnt) / n), (int)(((long long)(k + 1) * cnt) / n),
-               split ? at.y + k : -1, at.x + k);
-      wg_first[at.x + k] = at.x + k;
-    }
+    put_chunks(at.x, u, g, cnt, n, split ? at.y : -1);
     if (split) {
       int* sp = plan + L.split + 4 * (int64_t)at.z;
       sp[0] = u;
