@@ -443,6 +443,65 @@ __device__ void plan_step(const PlanArgs& a) {
   }
   atomicAdd(&s_hash, my_hash);
   __syncthreads();
+  // At most 64 (unit, kv head) pairs: wave 0 plans alone (below) while the other waves write
+  // a fused step's classes and page entries.
+  const bool one_wave = units * hkv <= 64;
+  // Tile classes, plan list entries and page entries of a fused step, from the packed
+  // per-unit counts, written by threads [t0, t0 + nthr) (nthr a multiple of 64).
+  auto fused_entries = [&](int t0, int nthr) {
+    {
+      const int me = tid - t0, wave = me >> 6, lane = me & 63;
+      for (int u = wave; u < units; u += nthr / 64) {
+        const int cw = s_upre[u], lw = s_nepre[u];
+        const int nc = cw & 0xffff, nfc = cw >> 16, nl = lw & 0xffff, nfl = lw >> 16;
+        int* list = plan + L.list + (int64_t)u * a.nkt;
+        for (int t = lane; t < a.nkt; t += 64) {
+          const int j = t - a.nct;   // live tile ordinal (negative for cached tiles)
+          const bool on = j < 0 ? t < nc : j < nl;
+          const bool full = j < 0 ? t < nfc : j < nfl;
+          const int cls = !on ? BCP_TILE_SKIP : full ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
+          if (a.tile_class) a.tile_class[(int64_t)u * a.nkt + t] = (uint8_t)cls;
+          if (on) list[j < 0 ? t : nc + j] = (t << 1) | (full ? 0 : 1);
+        }
+      }
+    }
+    if (a.phys_page) {
+      // Entry (sq, t, k) is the page of row t*tile_k + k*page_size; when pages tile the key
+      // tiles exactly that row is e*page_size for the entry's ordinal e inside its sequence.
+      // The loads of a batch of entries are issued before any of their stores.
+      const int me = tid - t0;
+      const int ppt = a.phys_per_tile, per_seq = a.nct * ppt, P = a.page_size;
+      const bool whole = a.tile_k % P == 0;
+      const int total = a.batch * per_seq;
+      constexpr int kB = 4;
+      for (int base = 0; base < total; base += kB * nthr) {
+        int pv[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = base + b * nthr + me;
+          pv[b] = -1;
+          if (idx < total) {
+            const int sq = idx / per_seq, e = idx - sq * per_seq;
+            int row, lp;
+            if (whole) {
+              row = e * P;
+              lp = e;
+            } else {
+              const int t = e / ppt, k = e - t * ppt;
+              row = t * a.tile_k + k * P;
+              lp = row / P;
+            }
+            if (row < s_seq[sq][2] && lp < a.max_pages) pv[b] = a.page_table[(int64_t)sq * a.max_pages + lp];
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = base + b * nthr + me;
+          if (idx < total) a.phys_page[idx] = pv[b] >= 0 && pv[b] < a.num_pages ? pv[b] : -1;
+        }
+      }
+    }
+  };
   if (a.fused) {
     // Mode A without a window (the host picks this only for such steps of at most
     // kFusedPlanElems classes and page entries, with the sequences in LDS). A committed key is
@@ -480,58 +539,10 @@ __device__ void plan_step(const PlanArgs& a) {
       s_nepre[u] = nl | (nfl << 16);
     }
     __syncthreads();
-    {
-      const int wave = tid >> 6, lane = tid & 63;
-      for (int u = wave; u < units; u += kPlanThreads / 64) {
-        const int cw = s_upre[u], lw = s_nepre[u];
-        const int nc = cw & 0xffff, nfc = cw >> 16, nl = lw & 0xffff, nfl = lw >> 16;
-        int* list = plan + L.list + (int64_t)u * a.nkt;
-        for (int t = lane; t < a.nkt; t += 64) {
-          const int j = t - a.nct;   // live tile ordinal (negative for cached tiles)
-          const bool on = j < 0 ? t < nc : j < nl;
-          const bool full = j < 0 ? t < nfc : j < nfl;
-          const int cls = !on ? BCP_TILE_SKIP : full ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
-          if (a.tile_class) a.tile_class[(int64_t)u * a.nkt + t] = (uint8_t)cls;
-          if (on) list[j < 0 ? t : nc + j] = (t << 1) | (full ? 0 : 1);
-        }
-      }
+    if (!one_wave) {
+      fused_entries(0, kPlanThreads);
+      __syncthreads();   // the counts (in the plan when they do not fit in LDS) are read below
     }
-    if (a.phys_page) {
-      // Entry (sq, t, k) is the page of row t*tile_k + k*page_size; when pages tile the key
-      // tiles exactly that row is e*page_size for the entry's ordinal e inside its sequence.
-      // The loads of a batch of entries are issued before any of their stores.
-      const int ppt = a.phys_per_tile, per_seq = a.nct * ppt, P = a.page_size;
-      const bool whole = tk % P == 0;
-      const int total = a.batch * per_seq;
-      constexpr int kB = 4;
-      for (int base = 0; base < total; base += kB * kPlanThreads) {
-        int pv[kB];
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-          const int idx = base + b * kPlanThreads + tid;
-          pv[b] = -1;
-          if (idx < total) {
-            const int sq = idx / per_seq, e = idx - sq * per_seq;
-            int row, lp;
-            if (whole) {
-              row = e * P;
-              lp = e;
-            } else {
-              const int t = e / ppt, k = e - t * ppt;
-              row = t * tk + k * P;
-              lp = row / P;
-            }
-            if (row < s_seq[sq][2] && lp < a.max_pages) pv[b] = a.page_table[(int64_t)sq * a.max_pages + lp];
-          }
-        }
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-          const int idx = base + b * kPlanThreads + tid;
-          if (idx < total) a.phys_page[idx] = pv[b] >= 0 && pv[b] < a.num_pages ? pv[b] : -1;
-        }
-      }
-    }
-    __syncthreads();   // the counts (in the plan when they do not fit in LDS) are read below
   }
   auto cnt_of = [&](int u) { return in_lds ? s_cnt[u] : plan[L.cnt + u]; };
   // Writes item `idx` (unit u, kv head g, ordinals [ob, oe), partial slot ps) with the
@@ -562,37 +573,6 @@ __device__ void plan_step(const PlanArgs& a) {
     }
   };
 
-  // Prefix sums of the per-unit tile counts.
-  const int upt = (units + kPlanThreads - 1) / kPlanThreads;
-  const int u0 = min(units, tid * upt), u1 = min(units, u0 + upt);
-  // (With them, the number of units with tiles before each unit.)
-  int mine = 0, mine_ne = 0;
-  for (int u = u0; u < u1; ++u) {
-    mine += cnt_of(u);
-    mine_ne += cnt_of(u) > 0;
-  }
-  Int3 tot;
-  const Int3 run3 = block_scan3_excl(Int3{mine, mine_ne, 0}, scan_lds, &tot);
-  int run = run3.x, run_ne = run3.y;
-  for (int u = u0; u < u1; ++u) {
-    plan[L.upre + u] = run;
-    if (in_lds) {
-      s_upre[u] = run;
-      s_nepre[u] = run_ne;
-    }
-    run += cnt_of(u);
-    run_ne += cnt_of(u) > 0;
-  }
-  const int total_tiles = tot.x;
-  if (tid == 0) plan[L.upre + units] = total_tiles;
-  for (int w = tid; w <= kWGs; w += kPlanThreads) wg_first[w] = INT32_MAX;
-  __syncthreads();   // upre is read back below by other threads
-  auto upre_of = [&](int u) { return in_lds ? s_upre[u] : plan[L.upre + u]; };
-
-  const unsigned W = (unsigned)total_tiles * (unsigned)hkv;
-  const int pairs = units * hkv;
-  unsigned n_wg = 1;
-  Int3 all = {0, 0, 0};
   // Items k = 0..n-1 of a pair of cnt visits cut into n near-equal chunks: chunk k covers
   // ordinals [floor(k*cnt/n), floor((k+1)*cnt/n)), stepped without a division per item.
   auto put_chunks = [&](int first, int u, int g, int cnt, int n, int slot0) {
@@ -626,48 +606,121 @@ __device__ void plan_step(const PlanArgs& a) {
     lo = new_lo;   // chunk counts fall as the length grows, so new_lo < new_hi
     hi = new_hi;
   };
-  if (pairs <= 64) {
-    // The decode path below with every pair on a lane of wave 0: its sums and its scan are
-    // wave operations, with no barrier (the other waves wait at the next one).
-    if (tid < 64) {
-      const int pr = tid;
-      const int u = pr < pairs ? pr % units : 0, g = pr < pairs ? pr / units : 0;
-      const int cnt = pr < pairs ? cnt_of(u) : 0;
-      const int cmax = wave_max_nonneg(cnt);
-      int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
-      if (cmax > c) {
-        int lo = c - 1, hi = cmax;
-        bool first = true;
-        while (hi - lo > 1) {
-          const int step = first ? 1 : (hi - lo + kCand) / (kCand + 1);
-          first = false;
-          int sums[kCand];
-#pragma unroll
-          for (int j = 0; j < kCand; ++j) {
-            const int cj = min(lo + step * (j + 1), hi);
-            sums[j] = wave_sum((cnt + cj - 1) / cj);
-          }
-          narrow(lo, hi, step, [&](int j) { return sums[j]; });
-        }
-        c = hi;
-      }
-      const int n = cnt > 0 ? (cnt + c - 1) / c : 0;
-      const bool split = n > 1;
-      const int in = wave_scan_incl(n), isp = wave_scan_incl(split ? n : 0), ip = wave_scan_incl(split ? 1 : 0);
-      all = Int3{__builtin_amdgcn_readlane(in, 63), __builtin_amdgcn_readlane(isp, 63),
-                 __builtin_amdgcn_readlane(ip, 63)};
-      const Int3 at = {in - n, isp - (split ? n : 0), ip - (split ? 1 : 0)};
-      put_chunks(at.x, u, g, cnt, n, split ? at.y : -1);
-      if (split) {
-        int* sp = plan + L.split + 4 * (int64_t)at.z;
-        sp[0] = u;
-        sp[1] = g;
-        sp[2] = at.y;
-        sp[3] = n;
-      }
-      n_wg = max(1, all.x);
+  // The header: item and split-pair counts, ranges, visits, tile sizes, then the words
+  // that the kernels and the host compare with their own arguments.
+  auto write_header = [&](int n_items, int n_split, unsigned n_ranges, int total_tiles) {
+    plan[0] = n_items;
+    plan[1] = n_split;
+    plan[2] = n_ranges;
+    plan[3] = total_tiles;
+    plan[4] = a.tile_q;
+    plan[5] = a.tile_k;
+    plan[6] = a.nqt;
+    plan[7] = a.nkt;
+    plan[kHdrMagic] = kPlanMagic;
+    plan[kHdrBatch] = a.batch;
+    plan[kHdrHkv] = a.num_kv_heads;
+    plan[kHdrLenHash] = (int)s_hash;
+    plan[kHdrWindow] = a.window;
+    plan[kHdrModeB] = a.mode_b;
+    plan[kHdrTotalQ] = a.total_q;
+    plan[kHdrKvCap] = a.kv_cap;
+  };
+  if (one_wave) {
+    if (tid >= 64) {
+      if (a.fused) fused_entries(64, kPlanThreads - 64);
+      return;
     }
-  } else if (pairs <= kPlanThreads) {
+    // The decode path below with every unit and every pair on a lane of wave 0: its sums and
+    // scans are wave operations, with no barrier.
+    const int lane = tid;
+    const int cu = lane < units ? cnt_of(lane) : 0;
+    const int cu_incl = wave_scan_incl(cu);
+    const int total_tiles = __builtin_amdgcn_readlane(cu_incl, 63);
+    if (lane < units) plan[L.upre + lane] = cu_incl - cu;
+    if (lane == 0) plan[L.upre + units] = total_tiles;
+    const unsigned W = (unsigned)total_tiles * (unsigned)hkv;
+    const int pairs = units * hkv;
+    const int pr = lane;
+    const int u = pr < pairs ? pr % units : 0, g = pr < pairs ? pr / units : 0;
+    const int cnt = pr < pairs ? cnt_of(u) : 0;
+    const int cmax = wave_max_nonneg(cnt);
+    int c = max(kMinChunk, (int)((W + kWGs - 1) / kWGs));
+    if (cmax > c) {
+      int lo = c - 1, hi = cmax;
+      bool first = true;
+      while (hi - lo > 1) {
+        const int step = first ? 1 : (hi - lo + kCand) / (kCand + 1);
+        first = false;
+        int sums[kCand];
+#pragma unroll
+        for (int j = 0; j < kCand; ++j) {
+          const int cj = min(lo + step * (j + 1), hi);
+          sums[j] = wave_sum((cnt + cj - 1) / cj);
+        }
+        narrow(lo, hi, step, [&](int j) { return sums[j]; });
+      }
+      c = hi;
+    }
+    const int n = cnt > 0 ? (cnt + c - 1) / c : 0;
+    const bool split = n > 1;
+    const int in = wave_scan_incl(n), isp = wave_scan_incl(split ? n : 0), ip = wave_scan_incl(split ? 1 : 0);
+    const int n_items = __builtin_amdgcn_readlane(in, 63);
+    put_chunks(in - n, u, g, cnt, n, split ? isp - n : -1);
+    if (split) {
+      int* sp = plan + L.split + 4 * (int64_t)(ip - 1);
+      sp[0] = u;
+      sp[1] = g;
+      sp[2] = isp - n;
+      sp[3] = n;
+    }
+    // Range r opens item r for every r below the item count and is empty after it, so its
+    // first item is min(r, items) (the suffix minimum of the general path, in closed form).
+    for (int w = lane; w <= kWGs; w += 64) {
+      const int f = min(w, n_items);
+      plan[L.wg + w] = f;
+      if (w < kWGs) {
+        plan[L.rng + kRngWords * (int64_t)w] = f;
+        plan[L.rng + kRngWords * (int64_t)w + 1] = min(w + 1, n_items);
+      }
+    }
+    if (lane == 0) write_header(n_items, __builtin_amdgcn_readlane(ip, 63), max(1, n_items), total_tiles);
+    return;
+  }
+
+  // Prefix sums of the per-unit tile counts.
+  const int upt = (units + kPlanThreads - 1) / kPlanThreads;
+  const int u0 = min(units, tid * upt), u1 = min(units, u0 + upt);
+  // (With them, the number of units with tiles before each unit.)
+  int mine = 0, mine_ne = 0;
+  for (int u = u0; u < u1; ++u) {
+    mine += cnt_of(u);
+    mine_ne += cnt_of(u) > 0;
+  }
+  Int3 tot;
+  const Int3 run3 = block_scan3_excl(Int3{mine, mine_ne, 0}, scan_lds, &tot);
+  int run = run3.x, run_ne = run3.y;
+  for (int u = u0; u < u1; ++u) {
+    plan[L.upre + u] = run;
+    if (in_lds) {
+      s_upre[u] = run;
+      s_nepre[u] = run_ne;
+    }
+    run += cnt_of(u);
+    run_ne += cnt_of(u) > 0;
+  }
+  const int total_tiles = tot.x;
+  if (tid == 0) plan[L.upre + units] = total_tiles;
+  for (int w = tid; w <= kWGs; w += kPlanThreads) wg_first[w] = INT32_MAX;
+  __syncthreads();   // upre is read back below by other threads
+  auto upre_of = [&](int u) { return in_lds ? s_upre[u] : plan[L.upre + u]; };
+
+  const unsigned W = (unsigned)total_tiles * (unsigned)hkv;
+  const int pairs = units * hkv;
+  unsigned n_wg = 1;
+  Int3 all = {0, 0, 0};
+
+  if (pairs <= kPlanThreads) {
     // Few (unit, kv head) pairs (decode batches): cut each pair into ceil(cnt/c) near-equal
     // chunks, one range each, with the smallest chunk length c >= max(kMinChunk,
     // ceil(W/kWGs)) that keeps the chunk count within kWGs (the count only falls as c
@@ -828,24 +881,7 @@ __device__ void plan_step(const PlanArgs& a) {
       plan[L.rng + kRngWords * (int64_t)w + 1] = wg_first[w + 1];
     }
   }
-  if (tid == 0) {
-    plan[0] = all.x;
-    plan[1] = all.z;
-    plan[2] = n_wg;
-    plan[3] = total_tiles;
-    plan[4] = a.tile_q;
-    plan[5] = a.tile_k;
-    plan[6] = a.nqt;
-    plan[7] = a.nkt;
-    plan[kHdrMagic] = kPlanMagic;
-    plan[kHdrBatch] = a.batch;
-    plan[kHdrHkv] = a.num_kv_heads;
-    plan[kHdrLenHash] = (int)s_hash;
-    plan[kHdrWindow] = a.window;
-    plan[kHdrModeB] = a.mode_b;
-    plan[kHdrTotalQ] = a.total_q;
-    plan[kHdrKvCap] = a.kv_cap;
-  }
+  if (tid == 0) write_header(all.x, all.z, n_wg, total_tiles);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void planner_kernel(PlanArgs a) { plan_step(a); }
