@@ -231,7 +231,7 @@ struct FastOffsets {
 };
 
 // Issue the direct loads of 8-row run q (rows 8q..8q+7) of a resolved tile into key stage
-// `sk` and value stage `sv`: NI K and NI V wave instructions, plus one block-id copy for
+// `sk` and value stage `sv` (whose LDS byte addresses are klds and vlds): NI K and NI V wave instructions, plus one block-id copy for
 // partial mode-B tiles. Returns the number of loads issued. When the run's 8 rows are
 // present and consecutive in memory (row0 >= 0), one wave-uniform base and fixed per-lane
 // offsets (fo, made for a run of the same parity) address them. Otherwise each lane
@@ -244,7 +244,8 @@ struct FastOffsets {
 // input is unspecified.
 template <int HD, int NI, bool BAND_B, class Smem>
 __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, const Stage st, Smem& sm,
-                                           int sk, int sv, const FastOffsets<HD>& fo, int q) {
+                                           int sk, int sv, unsigned klds, unsigned vlds,
+                                           const FastOffsets<HD>& fo, int q) {
   using D = DmaShape<HD>;
   if (st.e < 0) return 0;
   const int vt = st.e >> 1;
@@ -259,8 +260,8 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int base = (run0 + k * D::RPI) * HD;
-      dma16s(kb + e0, fo.k[k], lds_addr(&sm.k[sk][base]));
-      dma16s(vb + e0, fo.v[k], lds_addr(&sm.v[sv][base]));
+      dma16s(kb + e0, fo.k[k], klds + 2u * base);
+      dma16s(vb + e0, fo.v[k], vlds + 2u * base);
     }
   } else if (st.row0 <= -2) {
     // Live rows in the pool whose run crosses a page boundary: the first `split` rows from
@@ -275,8 +276,8 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       const int rr = k * D::RPI + lane / D::CPR, r = run0 + rr, pch = lane % D::CPR;
       const int64_t row = rr < split ? row0 + rr : row1 + rr;
       const int base = (run0 + k * D::RPI) * HD;
-      dma16(kb + (row * a.Hkv + it.g) * HD + 8 * (pch ^ kswz<HD>(r)), lds_addr(&sm.k[sk][base]));
-      dma16(vb + (row * a.Hkv + it.g) * HD + 8 * (pch ^ vswz<HD>(r)), lds_addr(&sm.v[sv][base]));
+      dma16(kb + (row * a.Hkv + it.g) * HD + 8 * (pch ^ kswz<HD>(r)), klds + 2u * base);
+      dma16(vb + (row * a.Hkv + it.g) * HD + 8 * (pch ^ vswz<HD>(r)), vlds + 2u * base);
     }
   } else {
     const int nvalid = tile_valid(a, it, vt);
@@ -312,8 +313,8 @@ __device__ __forceinline__ int stage_fetch(const AttnArgs& a, const Item& it, co
       const uint16_t* ksrc = ok ? kb + (row * a.Hkv + it.g) * HD : ksub;
       const uint16_t* vsrc = ok ? vb + (row * a.Hkv + it.g) * HD : vsub;
       const int base = (run0 + k * D::RPI) * HD;
-      dma16(ksrc + 8 * (pch ^ kswz<HD>(r)), lds_addr(&sm.k[sk][base]));
-      dma16(vsrc + 8 * (pch ^ vswz<HD>(r)), lds_addr(&sm.v[sv][base]));
+      dma16(ksrc + 8 * (pch ^ kswz<HD>(r)), klds + 2u * base);
+      dma16(vsrc + 8 * (pch ^ vswz<HD>(r)), vlds + 2u * base);
     }
   }
   // Block ids of a partial tile's keys: each wave handles its own 8 rows (lanes 0..7).
@@ -471,6 +472,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = HD / 16;       // MFMA steps over d for the scores
   constexpr int NDB = HD / 32;      // 32-row d blocks of O^T
   __shared__ __attribute__((aligned(16))) AttnSmem<HD> sm;
+  // LDS byte addresses of the first key and value stages.
+  const unsigned k_lds0 = lds_addr(&sm.k[0][0]), v_lds0 = lds_addr(&sm.v[0][0]);
+  constexpr unsigned kKStageBytes = sizeof(sm.k[0]), kVStageBytes = sizeof(sm.v[0]);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hl = lane >> 5;
@@ -630,8 +634,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       int issued = 0;
       for (int x = 0; x < lead; ++x) {
         const Stage st = meta_resolve(meta_read(x, nt, wave, sm));
-        issued = stage_fetch<HD, NI, BAND_B>(a, it, st, sm, x % kKStages, x % kVStages, fo, uni(wave));
+        issued = stage_fetch<HD, NI, BAND_B>(a, it, st, sm, x % kKStages, x % kVStages, k_lds0 + (x % kKStages) * kKStageBytes,
+                                             v_lds0 + (x % kVStages) * kVStageBytes, fo, uni(wave));
       }
+      // Stages of tile lead, the next to issue, advanced by one per vector phase.
+      int xk = lead % kKStages, xv = lead % kVStages;
       RawMeta raw = meta_read(lead, nt, wave, sm);         // next tile to issue
       int e_next = sm.win_e[0];                            // entry of the next tile to mask
       wait_vm(issued);
@@ -698,8 +705,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       auto vector_phase = [&](int t) {
         {
           const int x = t + lead;
-          issued = stage_fetch<HD, NI, BAND_B>(a, it, meta_resolve(raw), sm, x % kKStages, x % kVStages, fo, uni(wave));
+          issued = stage_fetch<HD, NI, BAND_B>(a, it, meta_resolve(raw), sm, xk, xv, k_lds0 + xk * kKStageBytes,
+                                               v_lds0 + xv * kVStageBytes, fo, uni(wave));
           raw = meta_read(x + 1, nt, wave, sm);
+          xk = xk == kKStages - 1 ? 0 : xk + 1;
+          xv = xv == kVStages - 1 ? 0 : xv + 1;
         }
         const int e_t = uni(e_next);
         e_next = sm.win_e[min(t + 1, kWin - 1)];   // used next phase, only if t+1 < nt
@@ -935,6 +945,9 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
   // Loads in flight per wave stay within the 6-bit counter: two pairs of tiles.
   static_assert(4 * kNRuns * (2 * NI + 2) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) NarrowSmem<HD> sm;
+  const unsigned k_lds0 = lds_addr(&sm.k[0][0]), v_lds0 = lds_addr(&sm.v[0][0]);
+  constexpr unsigned kNStageBytes = sizeof(sm.k[0]);
+  static_assert(sizeof(sm.k[0]) == sizeof(sm.v[0]), "one stage size for keys and values");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hl = lane >> 5;
@@ -1069,7 +1082,9 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
         for (int j = 0; j < kNRuns; ++j) {
           const int q = uni(wave) * kNRuns + j;
           const Stage st = meta_resolve(meta_read(x, nt, q, sm));
-          n += stage_fetch<HD, NI, BAND_B>(a, it, st, sm, x % kNStages, x % kNStages, fo[j & 1], q);
+          const int sx = x % kNStages;
+          n += stage_fetch<HD, NI, BAND_B>(a, it, st, sm, sx, sx, k_lds0 + sx * kNStageBytes, v_lds0 + sx * kNStageBytes,
+                                           fo[j & 1], q);
         }
         return n;
       };
