@@ -52,17 +52,21 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     float lc[MAXC];
     f32x4 oc[MAXC];
 #pragma unroll
-    for (int k = 0; k < MAXC; ++k) {
-      const int64_t slot = ps0 + min(k, n - 1);
-      lc[k] = a.part_lse[slot * kRowsPerWG + rho];
-      oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+    for (int k = 0; k < MAXC; ++k) {   // only the pair's own slots (n is uniform)
+      lc[k] = -INFINITY;
+      oc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < n) {
+        const int64_t slot = ps0 + k;
+        lc[k] = a.part_lse[slot * kRowsPerWG + rho];
+        oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+      }
     }
     int q0, q_len;
     live_rows(a.cu_q, s, a.total_q, a.max_q_len, &q0, &q_len);
     const int pos = r * a.tile_q + rho / a.G, hh = rho - (rho / a.G) * a.G;
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < MAXC; ++k) M = fmaxf(M, lc[k]);   // repeats of the last split change nothing
+    for (int k = 0; k < MAXC; ++k) M = fmaxf(M, lc[k]);   // absent slots hold -inf
     for (int c = MAXC; c < n; ++c) M = fmaxf(M, a.part_lse[(int64_t)(ps0 + c) * kRowsPerWG + rho]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
