@@ -37,6 +37,7 @@ CASES = [
     dict(seed=86, G=16, d=64, D=1, P=3, max_q=4, max_kv=200, batch=7),
     dict(seed=87, G=4, d=128, D=1, P=16, mode="B", max_q=16, max_kv=600),
     dict(seed=88, G=4, d=64, D=1, P=32, max_q=9, max_kv=5000, batch=4),       # long caches, split items
+    dict(seed=94, G=8, d=64, D=1, P=16, max_q=8, max_kv=2500, batch=9),       # several items per workgroup
     # block ids in promotion order (no order among live or committed rows)
     dict(seed=92, G=4, d=128, D=1, P=16, mode="Bu", max_q=16, max_kv=600),
     dict(seed=93, G=16, d=64, D=1, P=8, mode="Bu", max_q=4, max_kv=3000, batch=5),
