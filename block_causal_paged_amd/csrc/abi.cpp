@@ -328,9 +328,10 @@ int run_classify_and_plan(const bcp_meta* m, const Geo& g, uint8_t* tile_class, 
   p.kv_cap = m->max_pages_per_seq * m->page_size;
   p.window = m->window;
   p.mode_b = g.mode_b ? 1 : 0;
-  // A small mode-A step without a window is classified by the planner itself: one launch.
+  // A small mode-A step (with or without a window) is classified by the planner itself: one
+  // launch.
   const int64_t elems = (int64_t)m->batch * g.nqt * g.nkt + (phys_page ? (int64_t)m->batch * g.nct * a.phys_per_tile : 0);
-  if (plan && !g.mode_b && m->window == 0 && m->batch <= 1024 && elems <= kFusedPlanElems) {
+  if (plan && !g.mode_b && m->batch <= 1024 && elems <= kFusedPlanElems) {
     p.fused = 1;
     p.nct = g.nct;
     p.block_size = m->block_size;

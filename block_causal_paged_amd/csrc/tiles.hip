@@ -407,6 +407,48 @@ __device__ Int3 block_scan3_excl(Int3 v, Int3* lds, Int3* total) {
   return Int3{before.x + s.x - v.x, before.y + s.y - v.y, before.z + s.z - v.z};
 }
 
+// Classes of a mode-A unit's key tiles in closed form (rows i0..i1-1 of a sequence with ql
+// live rows and kvl committed ones; `window` 0 for none). In each region the non-skipped
+// tiles are a run: cached tiles [t_lo, nc), live tiles [l_lo, nl); the FULL ones among them
+// are the cached tiles in [tf_lo, nfc) and the live tiles in [lf_lo, nfl). Without a window
+// a committed key is seen by every live row, so cached tile t is non-skipped when it holds a
+// key and FULL when it holds tile_k; live tile j is non-skipped when its first key's block is
+// at most the last row's block qmax, FULL when its tile_k keys exist and lie in blocks no
+// later than the first row's block qmin. The window (query row i at position kvl + i,
+// committed key j at j, live key j at kvl + j; seen while fewer than W positions behind)
+// removes the tiles whose last key lies W or more positions before row i0, and leaves FULL
+// only the tiles whose first key is fewer than W positions before row i1 - 1.
+struct ModeABounds {
+  int t_lo, nc, tf_lo, nfc, l_lo, nl, lf_lo, nfl;
+};
+__device__ ModeABounds mode_a_bounds(const PlanArgs& a, int ql, int kvl, int i0, int i1) {
+  ModeABounds b = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (i1 <= i0) return b;
+  const int tk = a.tile_k, D = a.block_size, nlt = a.nkt - a.nct;
+  b.nc = min((kvl + tk - 1) / tk, a.nct);
+  b.nfc = min(kvl / tk, a.nct);
+  const int64_t qmax = (i1 - 1) / D, qmin = i0 / D;
+  const int reach = (int)min<int64_t>((qmax + 1) * D, ql);   // keys a row of the q-tile may see
+  const int full = (int)min<int64_t>((qmin + 1) * D, ql);    // keys every row of it sees
+  b.nl = min((reach + tk - 1) / tk, nlt);
+  b.nfl = min(full / tk, b.nl);
+  if (a.window > 0) {
+    const int64_t W = a.window;
+    // First tile whose last key (at most the region's last) is within W of row i0.
+    auto first_in = [&](int64_t last_key, int64_t need) -> int {   // need: that key's least index
+      if (last_key < need) return INT32_MAX;
+      const int64_t x = need + 1 - tk;                                  // t*tk + tk - 1 >= need
+      return x <= 0 ? 0 : (int)((x + tk - 1) / tk);
+    };
+    auto first_full = [&](int64_t x) -> int { return x < 0 ? 0 : (int)(x / tk) + 1; };   // t*tk > x
+    b.t_lo = min(first_in(kvl - 1, (int64_t)kvl + i0 - W + 1), b.nc);
+    b.tf_lo = first_full((int64_t)kvl + i1 - 1 - W);
+    b.l_lo = min(first_in(ql - 1, (int64_t)i0 - W + 1), b.nl);
+    b.lf_lo = first_full((int64_t)i1 - 1 - W);
+  }
+  return b;
+}
+
 // One workgroup turns the per-unit tile counts into the ranges of the step's visits and
 // the items (whole or partial (unit, kv head) pairs) that make them up. Each thread takes
 // a contiguous run of units, then of pairs, so one scan orders everything.
@@ -446,22 +488,23 @@ __device__ void plan_step(const PlanArgs& a) {
   // At most 64 (unit, kv head) pairs: wave 0 plans alone (below) while the other waves write
   // a fused step's classes and page entries.
   const bool one_wave = units * hkv <= 64;
-  // Tile classes, plan list entries and page entries of a fused step, from the packed
-  // per-unit counts, written by threads [t0, t0 + nthr) (nthr a multiple of 64).
+  // Tile classes, plan list entries and page entries of a fused step (each unit's classes
+  // from mode_a_bounds, one unit per wave), written by threads [t0, t0 + nthr) (nthr a
+  // multiple of 64).
   auto fused_entries = [&](int t0, int nthr) {
     {
       const int me = tid - t0, wave = me >> 6, lane = me & 63;
       for (int u = wave; u < units; u += nthr / 64) {
-        const int cw = s_upre[u], lw = s_nepre[u];
-        const int nc = cw & 0xffff, nfc = cw >> 16, nl = lw & 0xffff, nfl = lw >> 16;
+        const int sq = u / a.nqt, i0 = (u - sq * a.nqt) * a.tile_q, ql = s_seq[sq][1];
+        const ModeABounds b = mode_a_bounds(a, ql, s_seq[sq][2], i0, min(i0 + a.tile_q, ql));
         int* list = plan + L.list + (int64_t)u * a.nkt;
         for (int t = lane; t < a.nkt; t += 64) {
           const int j = t - a.nct;   // live tile ordinal (negative for cached tiles)
-          const bool on = j < 0 ? t < nc : j < nl;
-          const bool full = j < 0 ? t < nfc : j < nfl;
+          const bool on = j < 0 ? t >= b.t_lo && t < b.nc : j >= b.l_lo && j < b.nl;
+          const bool full = j < 0 ? t >= b.tf_lo && t < b.nfc : j >= b.lf_lo && j < b.nfl;
           const int cls = !on ? BCP_TILE_SKIP : full ? BCP_TILE_FULL : BCP_TILE_PARTIAL;
           if (a.tile_class) a.tile_class[(int64_t)u * a.nkt + t] = (uint8_t)cls;
-          if (on) list[j < 0 ? t : nc + j] = (t << 1) | (full ? 0 : 1);
+          if (on) list[j < 0 ? t - b.t_lo : b.nc - b.t_lo + j - b.l_lo] = (t << 1) | (full ? 0 : 1);
         }
       }
     }
@@ -503,40 +546,16 @@ __device__ void plan_step(const PlanArgs& a) {
     }
   };
   if (a.fused) {
-    // Mode A without a window (the host picks this only for such steps of at most
-    // kFusedPlanElems classes and page entries, with the sequences in LDS). A committed key is
-    // seen by every live row, so cached tile t is FULL when all tile_k of its keys exist,
-    // PARTIAL when some do, SKIP when none; live tile j (keys lo..hi) is SKIP when it has no
-    // key or its first key's block lo/D lies after the q-tile's last row's block, FULL when
-    // its last key's block is at most the q-tile's first row's block and it has all tile_k
-    // keys, PARTIAL otherwise. In both regions the non-skipped tiles are a prefix, so a
-    // tile's place in its unit's list follows from the counts without a scan.
-    // Per unit, four counts: its non-skipped cached tiles nc, the first nfc of them FULL (all
-    // tile_k keys committed), and its non-skipped live tiles nl, the first nfl of them FULL.
-    // Live tile j is non-skipped when its first key j*tile_k lies in a block no later than
-    // the q-tile's last row's block qmax, i.e. j*tile_k < (qmax+1)*D; it is FULL when it has
-    // tile_k keys all in blocks no later than the first row's block qmin, i.e.
-    // (j+1)*tile_k <= min(q_len, (qmin+1)*D). A fused step has at most kFusedPlanElems
-    // tiles, so each pair of counts packs into one word of the (not yet used) scan arrays.
-    const int tq = a.tile_q, tk = a.tile_k, D = a.block_size, nlt = a.nkt - a.nct;
+    // Mode A (the host picks this only for such steps of at most kFusedPlanElems classes and
+    // page entries, with the sequences in LDS): each unit's classes follow from its lengths
+    // (mode_a_bounds), and a tile's place in its unit's list from the same bounds, without a
+    // scan.
     for (int u = tid; u < units; u += kPlanThreads) {
-      const int sq = u / a.nqt, r = u - sq * a.nqt;
-      const int ql = s_seq[sq][1], kvl = s_seq[sq][2];
-      const int i0 = r * tq, i1 = min(i0 + tq, ql);
-      int nc = 0, nfc = 0, nl = 0, nfl = 0;
-      if (i1 > i0) {
-        nc = min((kvl + tk - 1) / tk, a.nct);
-        nfc = min(kvl / tk, a.nct);
-        const int64_t qmax = (i1 - 1) / D, qmin = i0 / D;
-        const int reach = (int)min<int64_t>((qmax + 1) * D, ql);   // keys a row of the q-tile may see
-        const int full = (int)min<int64_t>((qmin + 1) * D, ql);    // keys every row of it sees
-        nl = min((reach + tk - 1) / tk, nlt);
-        nfl = min(full / tk, nl);
-      }
-      plan[L.cnt + u] = nc + nl;
-      s_cnt[u] = nc + nl;
-      s_upre[u] = nc | (nfc << 16);
-      s_nepre[u] = nl | (nfl << 16);
+      const int sq = u / a.nqt, i0 = (u - sq * a.nqt) * a.tile_q, ql = s_seq[sq][1];
+      const ModeABounds b = mode_a_bounds(a, ql, s_seq[sq][2], i0, min(i0 + a.tile_q, ql));
+      const int cnt = (b.nc - b.t_lo) + (b.nl - b.l_lo);
+      plan[L.cnt + u] = cnt;
+      s_cnt[u] = cnt;
     }
     __syncthreads();
     if (!one_wave) {
