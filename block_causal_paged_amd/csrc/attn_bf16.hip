@@ -457,16 +457,24 @@ __device__ __forceinline__ void run_rows(const AttnArgs& a, const Item& it, cons
 // BAND_B: mode B with a sliding window (keys' positions staged beside their block ids).
 // LEAN: mode A without a window, live rows passed in (the decode and prefill shapes); the
 // other paths' state and branches drop out of the tile loop, which frees registers.
+// LEAN_B: likewise for mode B without a window, live rows passed in (multi-canvas decoding).
 __device__ __forceinline__ void make_lean(AttnArgs& a) {
   a.mode_b = 0;
   a.window = 0;
   a.live_in_cache = 0;
   a.q_blk = a.kv_blk = a.q_pos = a.kv_pos = nullptr;
 }
+__device__ __forceinline__ void make_lean_b(AttnArgs& a) {
+  a.mode_b = 1;
+  a.window = 0;
+  a.live_in_cache = 0;
+  a.q_pos = a.kv_pos = nullptr;
+}
 
-template <int HD, bool BAND_B, bool LEAN>
+template <int HD, bool BAND_B, bool LEAN, bool LEAN_B = false>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   if constexpr (LEAN) make_lean(a);
+  if constexpr (LEAN_B) make_lean_b(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16;       // MFMA steps over d for the scores
@@ -936,9 +944,10 @@ __device__ __forceinline__ void wait_vm_in(int n) {
   }
 }
 
-template <int HD, bool BAND_B, bool LEAN>
+template <int HD, bool BAND_B, bool LEAN, bool LEAN_B = false>
 __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a) {
   if constexpr (LEAN) make_lean(a);
+  if constexpr (LEAN_B) make_lean_b(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16, NDB = HD / 32;
@@ -1271,14 +1280,17 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
   const bool band_b = a.mode_b && a.window > 0;
   const bool lean = !a.mode_b && a.window == 0 && !a.live_in_cache;
+  const bool lean_b = a.mode_b && a.window == 0 && !a.live_in_cache;
   const dim3 g(grid), b(kThreads);
   if (head_dim == 128) {
     if (lean) hipLaunchKernelGGL((attn_bf16_kernel<128, false, true>), g, b, 0, stream, a);
     else if (band_b) hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), g, b, 0, stream, a);
+    else if (lean_b) hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true>), g, b, 0, stream, a);
     else hipLaunchKernelGGL((attn_bf16_kernel<128, false, false>), g, b, 0, stream, a);
   } else {
     if (lean) hipLaunchKernelGGL((attn_bf16_kernel<64, false, true>), g, b, 0, stream, a);
     else if (band_b) hipLaunchKernelGGL((attn_bf16_kernel<64, true, false>), g, b, 0, stream, a);
+    else if (lean_b) hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true>), g, b, 0, stream, a);
     else hipLaunchKernelGGL((attn_bf16_kernel<64, false, false>), g, b, 0, stream, a);
   }
   return hipGetLastError();
@@ -1287,14 +1299,17 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream
 hipError_t launch_attn_bf16_narrow(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
   const bool band_b = a.mode_b && a.window > 0;
   const bool lean = !a.mode_b && a.window == 0 && !a.live_in_cache;
+  const bool lean_b = a.mode_b && a.window == 0 && !a.live_in_cache;
   const dim3 g(grid), b(kNThreads);
   if (head_dim == 128) {
     if (lean) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, true>), g, b, 0, stream, a);
     else if (band_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, true, false>), g, b, 0, stream, a);
+    else if (lean_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, false, true>), g, b, 0, stream, a);
     else hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, false>), g, b, 0, stream, a);
   } else {
     if (lean) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, true>), g, b, 0, stream, a);
     else if (band_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, true, false>), g, b, 0, stream, a);
+    else if (lean_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, false, true>), g, b, 0, stream, a);
     else hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, false>), g, b, 0, stream, a);
   }
   return hipGetLastError();
