@@ -455,26 +455,32 @@ __device__ __forceinline__ void run_rows(const AttnArgs& a, const Item& it, cons
 // the loads of tile x+3 (keys) or x+4 (values) start in H(2x+2) or later: three key
 // stages and four value stages suffice.
 // BAND_B: mode B with a sliding window (keys' positions staged beside their block ids).
-// LEAN: mode A without a window, live rows passed in (the decode and prefill shapes); the
-// other paths' state and branches drop out of the tile loop, which frees registers.
-// LEAN_B: likewise for mode B without a window, live rows passed in (multi-canvas decoding).
-__device__ __forceinline__ void make_lean(AttnArgs& a) {
-  a.mode_b = 0;
-  a.window = 0;
-  a.live_in_cache = 0;
-  a.q_blk = a.kv_blk = a.q_pos = a.kv_pos = nullptr;
-}
-__device__ __forceinline__ void make_lean_b(AttnArgs& a) {
-  a.mode_b = 1;
-  a.window = 0;
+// Kernel instances (KIND). Each lean kind pins some arguments at entry, so that the other
+// paths' state and branches drop out of the tile loop, which frees registers; all take the
+// live rows passed in. kLeanA: mode A without a window (the decode and prefill shapes; its
+// plan entries follow from the unit's lengths). kLeanB: mode B without a window
+// (multi-canvas decoding). kLeanAW: mode A with a window. kGeneral: anything else (live rows
+// read from the pool).
+enum : int { kGeneral = 0, kLeanA = 1, kLeanB = 2, kLeanAW = 3 };
+template <int KIND>
+__device__ __forceinline__ void pin_kind(AttnArgs& a) {
+  if constexpr (KIND == kGeneral) return;
   a.live_in_cache = 0;
   a.q_pos = a.kv_pos = nullptr;
+  a.mode_b = KIND == kLeanB ? 1 : 0;
+  if constexpr (KIND != kLeanAW) a.window = 0;
+  if constexpr (KIND != kLeanB) a.q_blk = a.kv_blk = nullptr;
+}
+__host__ __device__ inline int kind_of(const AttnArgs& a, bool band_b) {
+  if (band_b || a.live_in_cache) return kGeneral;
+  if (a.mode_b) return a.window == 0 ? kLeanB : kGeneral;
+  return a.window == 0 ? kLeanA : kLeanAW;
 }
 
-template <int HD, bool BAND_B, bool LEAN, bool LEAN_B = false>
+template <int HD, bool BAND_B, int KIND>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
-  if constexpr (LEAN) make_lean(a);
-  if constexpr (LEAN_B) make_lean_b(a);
+  constexpr bool LEAN = KIND == kLeanA;
+  pin_kind<KIND>(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16;       // MFMA steps over d for the scores
@@ -944,10 +950,10 @@ __device__ __forceinline__ void wait_vm_in(int n) {
   }
 }
 
-template <int HD, bool BAND_B, bool LEAN, bool LEAN_B = false>
+template <int HD, bool BAND_B, int KIND>
 __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a) {
-  if constexpr (LEAN) make_lean(a);
-  if constexpr (LEAN_B) make_lean_b(a);
+  constexpr bool LEAN = KIND == kLeanA;
+  pin_kind<KIND>(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
   constexpr int NT = HD / 16, NDB = HD / 32;
@@ -1277,42 +1283,41 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
 
 }  // namespace
 
+// One launcher per kernel: the head_dim, the mode-B band flag and the instance kind pick the
+// template instance.
+#define BCP_LAUNCH_KIND(KERNEL, HD, THREADS)                                                             \
+  switch (kind) {                                                                                       \
+    case kLeanA: hipLaunchKernelGGL((KERNEL<HD, false, kLeanA>), g, dim3(THREADS), 0, stream, a); break;   \
+    case kLeanB: hipLaunchKernelGGL((KERNEL<HD, false, kLeanB>), g, dim3(THREADS), 0, stream, a); break;   \
+    case kLeanAW: hipLaunchKernelGGL((KERNEL<HD, false, kLeanAW>), g, dim3(THREADS), 0, stream, a); break; \
+    default:                                                                                            \
+      if (band_b) hipLaunchKernelGGL((KERNEL<HD, true, kGeneral>), g, dim3(THREADS), 0, stream, a);      \
+      else hipLaunchKernelGGL((KERNEL<HD, false, kGeneral>), g, dim3(THREADS), 0, stream, a);            \
+  }
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
   const bool band_b = a.mode_b && a.window > 0;
-  const bool lean = !a.mode_b && a.window == 0 && !a.live_in_cache;
-  const bool lean_b = a.mode_b && a.window == 0 && !a.live_in_cache;
-  const dim3 g(grid), b(kThreads);
+  const int kind = kind_of(a, band_b);
+  const dim3 g(grid);
   if (head_dim == 128) {
-    if (lean) hipLaunchKernelGGL((attn_bf16_kernel<128, false, true>), g, b, 0, stream, a);
-    else if (band_b) hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), g, b, 0, stream, a);
-    else if (lean_b) hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, false, false>), g, b, 0, stream, a);
+    BCP_LAUNCH_KIND(attn_bf16_kernel, 128, kThreads)
   } else {
-    if (lean) hipLaunchKernelGGL((attn_bf16_kernel<64, false, true>), g, b, 0, stream, a);
-    else if (band_b) hipLaunchKernelGGL((attn_bf16_kernel<64, true, false>), g, b, 0, stream, a);
-    else if (lean_b) hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, false, false>), g, b, 0, stream, a);
+    BCP_LAUNCH_KIND(attn_bf16_kernel, 64, kThreads)
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16_narrow(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
   const bool band_b = a.mode_b && a.window > 0;
-  const bool lean = !a.mode_b && a.window == 0 && !a.live_in_cache;
-  const bool lean_b = a.mode_b && a.window == 0 && !a.live_in_cache;
-  const dim3 g(grid), b(kNThreads);
+  const int kind = kind_of(a, band_b);
+  const dim3 g(grid);
   if (head_dim == 128) {
-    if (lean) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, true>), g, b, 0, stream, a);
-    else if (band_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, true, false>), g, b, 0, stream, a);
-    else if (lean_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, false, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_narrow_kernel<128, false, false>), g, b, 0, stream, a);
+    BCP_LAUNCH_KIND(attn_bf16_narrow_kernel, 128, kNThreads)
   } else {
-    if (lean) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, true>), g, b, 0, stream, a);
-    else if (band_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, true, false>), g, b, 0, stream, a);
-    else if (lean_b) hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, false, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_narrow_kernel<64, false, false>), g, b, 0, stream, a);
+    BCP_LAUNCH_KIND(attn_bf16_narrow_kernel, 64, kNThreads)
   }
   return hipGetLastError();
 }
+#undef BCP_LAUNCH_KIND
 
 }  // namespace bcp
