@@ -456,30 +456,34 @@ __device__ __forceinline__ void run_rows(const AttnArgs& a, const Item& it, cons
 // stages and four value stages suffice.
 // BAND_B: mode B with a sliding window (keys' positions staged beside their block ids).
 // Kernel instances (KIND). Each lean kind pins some arguments at entry, so that the other
-// paths' state and branches drop out of the tile loop, which frees registers; all take the
-// live rows passed in. kLeanA: mode A without a window (the decode and prefill shapes; its
-// plan entries follow from the unit's lengths). kLeanB: mode B without a window
-// (multi-canvas decoding). kLeanAW: mode A with a window. kGeneral: anything else (live rows
-// read from the pool).
-enum : int { kGeneral = 0, kLeanA = 1, kLeanB = 2, kLeanAW = 3 };
+// paths' state and branches drop out of the tile loop, which frees registers. kLeanA: mode A
+// without a window, live rows passed in (the decode and prefill shapes). kLeanB: mode B
+// without a window (multi-canvas decoding). kLeanAW: mode A with a window. kLeanAL, kLeanBL:
+// mode A or B without a window, live rows read from the pool. In mode A without a window the
+// plan entries follow from the unit's lengths (kLeanA, kLeanAL). kGeneral: anything else (a
+// window together with live rows in the pool, or mode B with a window, which has its own
+// band flag).
+enum : int { kGeneral = 0, kLeanA = 1, kLeanB = 2, kLeanAW = 3, kLeanAL = 4, kLeanBL = 5 };
 template <int KIND>
 __device__ __forceinline__ void pin_kind(AttnArgs& a) {
   if constexpr (KIND == kGeneral) return;
-  a.live_in_cache = 0;
+  constexpr bool mb = KIND == kLeanB || KIND == kLeanBL;
+  a.live_in_cache = KIND == kLeanAL || KIND == kLeanBL ? 1 : 0;
   a.q_pos = a.kv_pos = nullptr;
-  a.mode_b = KIND == kLeanB ? 1 : 0;
+  a.mode_b = mb ? 1 : 0;
   if constexpr (KIND != kLeanAW) a.window = 0;
-  if constexpr (KIND != kLeanB) a.q_blk = a.kv_blk = nullptr;
+  if constexpr (!mb) a.q_blk = a.kv_blk = nullptr;
 }
 __host__ __device__ inline int kind_of(const AttnArgs& a, bool band_b) {
-  if (band_b || a.live_in_cache) return kGeneral;
+  if (band_b) return kGeneral;
+  if (a.live_in_cache) return a.window != 0 ? kGeneral : a.mode_b ? kLeanBL : kLeanAL;
   if (a.mode_b) return a.window == 0 ? kLeanB : kGeneral;
   return a.window == 0 ? kLeanA : kLeanAW;
 }
 
 template <int HD, bool BAND_B, int KIND>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
-  constexpr bool LEAN = KIND == kLeanA;
+  constexpr bool LEAN = KIND == kLeanA || KIND == kLeanAL;   // plan entries from the lengths
   pin_kind<KIND>(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
@@ -952,7 +956,7 @@ __device__ __forceinline__ void wait_vm_in(int n) {
 
 template <int HD, bool BAND_B, int KIND>
 __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a) {
-  constexpr bool LEAN = KIND == kLeanA;
+  constexpr bool LEAN = KIND == kLeanA || KIND == kLeanAL;   // plan entries from the lengths
   pin_kind<KIND>(a);
   using D = DmaShape<HD>;
   constexpr int NI = D::NI;
@@ -1290,6 +1294,8 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
     case kLeanA: hipLaunchKernelGGL((KERNEL<HD, false, kLeanA>), g, dim3(THREADS), 0, stream, a); break;   \
     case kLeanB: hipLaunchKernelGGL((KERNEL<HD, false, kLeanB>), g, dim3(THREADS), 0, stream, a); break;   \
     case kLeanAW: hipLaunchKernelGGL((KERNEL<HD, false, kLeanAW>), g, dim3(THREADS), 0, stream, a); break; \
+    case kLeanAL: hipLaunchKernelGGL((KERNEL<HD, false, kLeanAL>), g, dim3(THREADS), 0, stream, a); break; \
+    case kLeanBL: hipLaunchKernelGGL((KERNEL<HD, false, kLeanBL>), g, dim3(THREADS), 0, stream, a); break; \
     default:                                                                                            \
       if (band_b) hipLaunchKernelGGL((KERNEL<HD, true, kGeneral>), g, dim3(THREADS), 0, stream, a);      \
       else hipLaunchKernelGGL((KERNEL<HD, false, kGeneral>), g, dim3(THREADS), 0, stream, a);            \
