@@ -467,6 +467,42 @@ __device__ void plan_step(const PlanArgs& a) {
   const bool seq_lds = a.batch <= kPlanLdsSeqs;
   if (in_lds && !a.fused)
     for (int u = tid; u < units; u += kPlanThreads) s_cnt[u] = plan[L.cnt + u];
+  // At most 64 (unit, kv head) pairs: wave 0 plans alone (below) while the other waves write
+  // a fused step's classes and page entries.
+  const bool one_wave = units * hkv <= 64;
+  // A fused step's page entries: the first batch of page-table loads is issued here, beside
+  // the length loads, for every entry inside max_pages_per_seq; which of them lie below the
+  // committed length is decided when they are stored. So the page entries cost no round
+  // trip of their own after the lengths.
+  constexpr int kB = 4;
+  const int pe_t0 = one_wave ? 64 : 0, pe_nthr = kPlanThreads - pe_t0;
+  int pe_first[kB];
+  auto page_entry = [&](int idx, int* sq, int* row, int* lp) {
+    const int ppt = a.phys_per_tile, per_seq = a.nct * ppt, P = a.page_size;
+    *sq = idx / per_seq;
+    const int e = idx - *sq * per_seq;
+    if (a.tile_k % P == 0) {
+      *row = e * P;
+      *lp = e;
+    } else {
+      const int t = e / ppt, k = e - t * ppt;
+      *row = t * a.tile_k + k * P;
+      *lp = *row / P;
+    }
+  };
+  if (a.fused && a.phys_page && tid >= pe_t0) {
+    const int total = a.batch * a.nct * a.phys_per_tile;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int idx = b * pe_nthr + tid - pe_t0;
+      pe_first[b] = -1;
+      if (idx < total) {
+        int sq, row, lp;
+        page_entry(idx, &sq, &row, &lp);
+        if (lp < a.max_pages) pe_first[b] = a.page_table[(int64_t)sq * a.max_pages + lp];
+      }
+    }
+  }
   // The header's length hash: the wrapping sum of every sequence's hash.
   __shared__ unsigned s_hash;
   if (tid == 0) s_hash = 0u;
@@ -485,9 +521,6 @@ __device__ void plan_step(const PlanArgs& a) {
   }
   atomicAdd(&s_hash, my_hash);
   __syncthreads();
-  // At most 64 (unit, kv head) pairs: wave 0 plans alone (below) while the other waves write
-  // a fused step's classes and page entries.
-  const bool one_wave = units * hkv <= 64;
   // Tile classes, plan list entries and page entries of a fused step (each unit's classes
   // from mode_a_bounds, one unit per wave), written by threads [t0, t0 + nthr) (nthr a
   // multiple of 64).
@@ -511,12 +544,10 @@ __device__ void plan_step(const PlanArgs& a) {
     if (a.phys_page) {
       // Entry (sq, t, k) is the page of row t*tile_k + k*page_size; when pages tile the key
       // tiles exactly that row is e*page_size for the entry's ordinal e inside its sequence.
-      // The loads of a batch of entries are issued before any of their stores.
+      // The loads of a batch of entries are issued before any of their stores; the first
+      // batch was loaded at the start (threads t0.. of this call are the ones that did).
       const int me = tid - t0;
-      const int ppt = a.phys_per_tile, per_seq = a.nct * ppt, P = a.page_size;
-      const bool whole = a.tile_k % P == 0;
-      const int total = a.batch * per_seq;
-      constexpr int kB = 4;
+      const int total = a.batch * a.nct * a.phys_per_tile;
       for (int base = 0; base < total; base += kB * nthr) {
         int pv[kB];
 #pragma unroll
@@ -524,17 +555,11 @@ __device__ void plan_step(const PlanArgs& a) {
           const int idx = base + b * nthr + me;
           pv[b] = -1;
           if (idx < total) {
-            const int sq = idx / per_seq, e = idx - sq * per_seq;
-            int row, lp;
-            if (whole) {
-              row = e * P;
-              lp = e;
-            } else {
-              const int t = e / ppt, k = e - t * ppt;
-              row = t * a.tile_k + k * P;
-              lp = row / P;
-            }
-            if (row < s_seq[sq][2] && lp < a.max_pages) pv[b] = a.page_table[(int64_t)sq * a.max_pages + lp];
+            int sq, row, lp;
+            page_entry(idx, &sq, &row, &lp);
+            if (base == 0) pv[b] = pe_first[b];
+            else if (lp < a.max_pages) pv[b] = a.page_table[(int64_t)sq * a.max_pages + lp];
+            if (row >= s_seq[sq][2]) pv[b] = -1;
           }
         }
 #pragma unroll
@@ -559,7 +584,7 @@ __device__ void plan_step(const PlanArgs& a) {
     }
     __syncthreads();
     if (!one_wave) {
-      fused_entries(0, kPlanThreads);
+      fused_entries(pe_t0, pe_nthr);
       __syncthreads();   // the counts (in the plan when they do not fit in LDS) are read below
     }
   }
@@ -647,7 +672,7 @@ __device__ void plan_step(const PlanArgs& a) {
   };
   if (one_wave) {
     if (tid >= 64) {
-      if (a.fused) fused_entries(64, kPlanThreads - 64);
+      if (a.fused) fused_entries(pe_t0, pe_nthr);
       return;
     }
     // The decode path below with every unit and every pair on a lane of wave 0: its sums and
