@@ -258,11 +258,11 @@ __device__ __forceinline__ PlanShape plan_shape(cint32* plan) {
   return h;
 }
 __device__ __forceinline__ bool plan_matches(const PlanShape& h, const AttnArgs& a) {
-  auto w = [&](int k) { return h.w[k - kHdrTileQ]; };
-  return (w(kHdrMagic) == kPlanMagic) & (w(kHdrTileQ) == a.tile_q) & (w(kHdrTileK) == kTileK) &
-         (w(kHdrNqt) == a.nqt) & (w(kHdrNkt) == a.nkt) & (w(kHdrBatch) == a.batch) & (w(kHdrHkv) == a.Hkv) &
-         (w(kHdrWindow) == a.window) & (w(kHdrModeB) == a.mode_b) & (w(kHdrTotalQ) == a.total_q) &
-         (w(kHdrKvCap) == a.max_pages * a.page_size);
+  // Every comparison is evaluated (no short-circuit branches): one scalar AND chain.
+  auto eq = [&](int k, int v) { return (int)(h.w[k - kHdrTileQ] == v); };
+  return (eq(kHdrMagic, kPlanMagic) & eq(kHdrTileQ, a.tile_q) & eq(kHdrTileK, kTileK) & eq(kHdrNqt, a.nqt) &
+          eq(kHdrNkt, a.nkt) & eq(kHdrBatch, a.batch) & eq(kHdrHkv, a.Hkv) & eq(kHdrWindow, a.window) &
+          eq(kHdrModeB, a.mode_b) & eq(kHdrTotalQ, a.total_q) & eq(kHdrKvCap, a.max_pages * a.page_size)) != 0;
 }
 __device__ __forceinline__ bool plan_matches(cint32* plan, const AttnArgs& a) {
   return plan_matches(plan_shape(plan), a);
