@@ -818,7 +818,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       vector_phase(0);
       __syncthreads();
       for (int t = 1; t < nt; ++t) {
+        // The wave in its matrix phase takes the SIMD's issue arbitration from the wave in its
+        // vector phase, so that the matrix instructions of the younger group are not held
+        // behind the older group's softmax; the four phases then last about as long.
+        __builtin_amdgcn_s_setprio(1);
         matrix_phase(t, std::true_type{}, std::true_type{});
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         vector_phase(t);
         __syncthreads();
