@@ -813,14 +813,17 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         wait_vm(issued);
       };
 
+      __builtin_amdgcn_s_setprio(1);
       matrix_phase(0, std::true_type{}, std::false_type{});
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       vector_phase(0);
       __syncthreads();
       for (int t = 1; t < nt; ++t) {
         // The wave in its matrix phase takes the SIMD's issue arbitration from the wave in its
-        // vector phase, so that the matrix instructions of the younger group are not held
-        // behind the older group's softmax; the four phases then last about as long.
+        // vector phase (here and in the item's first and last matrix phase), so that the matrix
+        // instructions of the younger group are not held behind the older group's softmax; the
+        // four phases then last about as long.
         __builtin_amdgcn_s_setprio(1);
         matrix_phase(t, std::true_type{}, std::true_type{});
         __builtin_amdgcn_s_setprio(0);
@@ -829,7 +832,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         __syncthreads();
       }
       // The last tile's PV product; group A then waits out group B's last vector phase.
+      __builtin_amdgcn_s_setprio(1);
       matrix_phase(nt, std::false_type{}, std::true_type{});
+      __builtin_amdgcn_s_setprio(0);
       if (!grp) __syncthreads();
     }   // window
 
