@@ -723,8 +723,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       auto vector_phase = [&](int t) {
         {
           const int x = t + lead;
+          // The loads go out at the matrix phase's priority, ahead of the other wave's
+          // instructions, so that they start their HBM round trip as early as possible.
+          __builtin_amdgcn_s_setprio(1);
           issued = stage_fetch<HD, NI, BAND_B>(a, it, meta_resolve(raw), sm, xk, xv, k_lds0 + xk * kKStageBytes,
                                                v_lds0 + xv * kVStageBytes, fo, uni(wave));
+          __builtin_amdgcn_s_setprio(0);
           raw = meta_read(x + 1, nt, wave, sm);
           xk = xk == kKStages - 1 ? 0 : xk + 1;
           xv = xv == kVStages - 1 ? 0 : xv + 1;
