@@ -1,9 +1,9 @@
 """KV commit: finished rows written into their cache pages (oracle; test infrastructure only).
 
-"Inference for Interpretable Text-Diffusion Models", section "KV Cache": completed
-prompt blocks are written to the cache at prefill, and after a decoded block is fully
-unmasked a final pass commits its keys and values to the cache. The cache is paged
-(section "Paged Attention"), so logical destination row j of sequence s is page
+"Inference for Interpretable Text-Diffusion Models", section "KV Cache" (steps 1 and 3):
+prefill stores the prompt's blocks in the cache, and a decoded block's keys and values
+are stored by a pass of their own once none of its positions is still undecided. The
+cache is paged (section "Paged Attention"), so logical destination row j of sequence s is page
 page_table[s, j // P], slot j % P. Entries in the multi-canvas arena also record their
 position tag beside the key and value ("Inference: Fewer, smaller forwards",
 Advancement 11); here the tags are the block id and, for sliding-window layers, the
