@@ -158,6 +158,64 @@ __device__ __forceinline__ float half_max(float x) {
 
 __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 
+// The same exchange for a sum: x[l % 32] + x[l % 32 + 32].
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// P = 2^(s * sl2 - m) of one 64-key tile for this lane's 32 scores, in bf16 for the PV
+// product; returns the lane's sum of the fp32 values (a tree per 8 keys).
+__device__ __forceinline__ float tile_exp(const f32x16 (&sc)[2], float sl2, float m, bf16x8 (&pf)[2][2]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hs + e], sl2, -m));
+      pf[kb][hs] = to_bf16x8(x);
+      rs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+    }
+  return rs;
+}
+
+// Online softmax of one tile (log2 domain), for the query row this lane holds half of.
+// The reference m is lazy: it starts at 0 and moves only when needed, and numerator (O)
+// and denominator (l) both use it, so the result is the softmax whatever its value. The
+// tile's P is first taken against the current m, and the row sum doubles as the check:
+// only when some lane's sum exceeds 2^16 (a value may have outgrown the reference) or a
+// row with no mass yet gets a sum below 2^-64 (its values may vanish) does the wave take
+// the row max (over both lane halves) and, where it is more than 2^8 above m or is the
+// row's first visible key, move m to it, rescale O and l, and take P again. So P <= 2^16
+// always (bf16 and the fp32 sums hold it with room to spare), and no per-tile max is
+// needed while the scores stay in range.
+constexpr float kSumHi = 65536.f, kSumLo = 0x1p-64f;
+template <int NDB>
+__device__ __forceinline__ void tile_softmax(const f32x16 (&sc)[2], float sl2, float& m, float& l, f32x16 (&o)[NDB],
+                                             bf16x8 (&pf)[2][2]) {
+  float rs = tile_exp(sc, sl2, m, pf);
+  const bool redo = !(rs <= kSumHi) || (l == 0.f && rs < kSumLo);
+  if (__builtin_amdgcn_ballot_w64(redo)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
+    const float mcand = half_max(mx) * sl2;   // -inf when no key of the tile is visible
+    const bool first = half_sum(l) == 0.f;    // no mass yet: O and l are 0
+    const bool grow = mcand > m + 8.f || (first && mcand != -INFINITY);
+    const float alpha = grow && !first ? __builtin_amdgcn_exp2f(m - mcand) : 1.f;
+    m = grow ? mcand : m;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    rs = tile_exp(sc, sl2, m, pf);
+  }
+  l += rs;
+}
+
 struct Item {
   int s, g, q0, q_len, kvl;
   int lp_live;   // logical page of row kv_len (the first live row when they sit in the pool)
@@ -620,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    float m = 0.f, l = 0.f;   // reference and row sum of the online softmax (tile_softmax)
     int n_partial = 0;
 
     for (int wb = ob; wb < oe; wb += kWin) {
@@ -777,39 +835,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
               }
           }
         }
-        // Online softmax in the log2 domain, with a lazy reference max: m only moves when
-        // a row's max grows by more than 2^8 (or on its first visible key). Numerator and
-        // denominator both use m, so the result is the same; P <= 2^8 fits bf16 easily.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
-        mx = half_max(mx);
-        const float mcand = mx * sl2;
-        const bool grow = mcand > m + 8.f;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          // Rows that do not grow keep alpha = 1 (their m may still be -inf).
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m - mcand) : 1.f;   // 0 if m was -inf
-          m = grow ? mcand : m;
-          l *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        }
-        const float muse = m == -INFINITY ? 0.f : m;
-        // P in bf16; the row sum adds the fp32 values, as a tree per 8 keys.
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
-            f32x8 x;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hs + e], sl2, -muse));
-            pf[kb][hs] = to_bf16x8(x);
-            rs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
-          }
-        l += rs;
+        tile_softmax<NDB>(sc, sl2, m, l, o, pf);
         // Keep the softmax ahead of the wait below (the compiler may not sink it past).
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -1150,7 +1176,10 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
               sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s == 0 ? f32x16{} : sc[kb], 0, 0, 0);
             }
         }
-        // Mask (partial tiles only) and online softmax, as in the wide kernel.
+        // Mask (partial tiles only) as in the wide kernel, then the online softmax with a
+        // lazy reference max: m moves only when a row's max grows by more than 2^8 (or on
+        // its first visible key). This kernel's per-tile chain (scores, softmax, PV) is
+        // latency-bound, and the row-sum check of tile_softmax measured slower here.
         const bool partial = e_t & 1;
         n_partial += partial;
         if (partial) {
