@@ -196,6 +196,49 @@ def test_attention_large_scores():
     assert_close(out, O_ref, "bf16", lse, L_ref, what="large-scores", abs_gate=False)
 
 
+def offset_score_case(seed, offsets, q_lens, kv_lens, G=4, Hkv=2, d=128, D=64, P=16):
+    """Scores shifted far from zero: every key (cached and live) carries a component c*u
+    along one unit direction u, and query head h a component a_h*u, so each score of head h
+    is offset by about offsets[h % len(offsets)] log2 units (after the 1/sqrt(d) scale) on
+    top of a spread of a few units. Far below zero the exponentials underflow against a
+    reference near 0; far above, they overflow: the online softmax has to move its
+    reference before it can use a tile."""
+    rng = np.random.default_rng(seed)
+    case = make_case(seed, dtype="bf16", num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=d, block_size=D,
+                     page_size=P, q_lens=q_lens, kv_lens=kv_lens, qkv_std=1 / np.sqrt(d), rng=rng)
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    c = np.float32(48.0)
+    sl2 = np.log2(np.e) / np.sqrt(d)
+    a = np.array([offsets[h % len(offsets)] / (sl2 * c) for h in range(G * Hkv)], dtype=np.float32)
+    case.q = bf16_bits(bf16_float(case.q) + a[None, :, None] * u)
+    case.k_new = bf16_bits(bf16_float(case.k_new) + c * u)
+    used = np.zeros(case.k_cache.shape[:2], dtype=bool)     # only mapped, committed slots
+    for s in range(case.batch):
+        j = np.arange(int(case.kv_len[s]))
+        used[case.page_table[s, j // P], j % P] = True
+    kc = bf16_float(case.k_cache)
+    kc[used] += c * u
+    case.k_cache = np.where(used[..., None, None], bf16_bits(np.nan_to_num(kc)), case.k_cache)
+    return case
+
+
+@pytest.mark.parametrize("offsets", [(-300.0,), (-100.0,), (300.0,), (-300.0, 300.0, 0.0, -90.0)],
+                         ids=["minus300", "minus100", "plus300", "mixed"])
+@pytest.mark.parametrize("narrow", [False, True], ids=["wide", "narrow"])
+def test_scores_far_from_zero(offsets, narrow):
+    """Rows whose scores all sit hundreds of log2 units below or above zero (and, mixed,
+    heads of either kind in one wave) match the oracle, which subtracts each row's true max.
+    Wide q-tiles (64 live rows per sequence) and narrow ones (at most 16 positions)."""
+    q_lens, kv_lens = ([64, 64, 40], [700, 129, 0]) if not narrow else ([9, 5, 16], [700, 129, 0])
+    case = offset_score_case(31 + len(offsets), offsets, q_lens, kv_lens)
+    dc = DeviceCase(case)
+    assert (bcp.num_q_tiles(bcp.StepMeta(**dc.meta_kwargs())) == 1) and (case.max_q_len * 4 <= 64) == narrow
+    O_ref, L_ref = oracle_attention(case)
+    out, lse = run_attn(dc)
+    assert_close(out, O_ref, "bf16", lse, L_ref, what=f"scores offset {offsets}")
+
+
 def test_large_scores_grow_across_tiles():
     """The stress case really moves the row max across tiles: for most query rows the max
     over each successive 64-key tile of the cached keys rises, and overall by > 8 log2 units."""
