@@ -361,9 +361,12 @@ def test_C5_long_context_every_sequence(workloads):
 
 
 def test_C3_prefill_sampled(workloads):
+    """The first and last row of every one of the 128 blocks of every sequence (each block
+    edge of the mask, from both sides) and 32 drawn rows per sequence."""
     case = workloads(3)
     rng = np.random.default_rng(3003)
-    rows = {s: np.unique(np.concatenate([[0, 63, 64, 8191], rng.integers(0, 8192, 28)])) for s in range(4)}
+    rows = {s: np.unique(np.concatenate([np.arange(0, 8192, 64), np.arange(63, 8192, 64), rng.integers(0, 8192, 32)]))
+            for s in range(4)}
     O_ref, L_ref = oracle_attention(case, rows=rows)
     out, lse = run_attn(DeviceCase(case))
     assert_close(out, O_ref, "bf16", lse, L_ref, what="C3 sampled")
