@@ -514,8 +514,14 @@ int attn_impl(const bcp_meta* m, const void* q, const void* k_new, const void* v
   a.v_cache = v_cache;
   a.out = out;
   a.lse = lse;
-  a.part_o = part ? (float*)ws : nullptr;
-  a.part_lse = part ? (float*)ws + (size_t)kMaxPartialSlots * kRowsPerWG * m->head_dim : nullptr;
+  // Split-KV partials: fp32 for fp32 steps; for bf16 steps fp16 rows in the first half of the
+  // same region and their row factors right after them (the fp32-sized region holds both).
+  const size_t part_elems = (size_t)kMaxPartialSlots * kRowsPerWG * m->head_dim;
+  const bool half_parts = m->dtype == BCP_BF16;
+  a.part_o = part && !half_parts ? (float*)ws : nullptr;
+  a.part_h = part && half_parts ? (uint16_t*)ws : nullptr;
+  a.part_scale = part && half_parts ? (float*)((uint16_t*)ws + part_elems) : nullptr;
+  a.part_lse = part ? (float*)ws + part_elems : nullptr;
   a.cu_q = m->cu_q;
   a.kv_len = m->kv_len;
   a.page_table = m->page_table;

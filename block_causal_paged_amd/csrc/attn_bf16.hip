@@ -46,6 +46,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -162,6 +164,18 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertv
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A split piece's partial output is stored in fp16, each row multiplied by a power of two
+// that puts its largest magnitude in [2^13, 2^14): fp16 then keeps 11 significant bits of
+// every value of the row that matters and cannot overflow, whatever the values' scale. amax
+// is the largest |O| of this lane's half of the row before the division by the row sum,
+// inv that division; returns the factor for this lane's values and sets *restore to what
+// the merge multiplies the stored row by.
+__device__ __forceinline__ float piece_factor(float amax, float inv, float* restore) {
+  const int e = clampi(__builtin_amdgcn_frexp_expf(half_max(amax) * inv), -100, 126);
+  *restore = __builtin_amdgcn_ldexpf(1.f, e - 14);
+  return __builtin_amdgcn_ldexpf(inv, 14 - e);
 }
 
 // P = 2^(s * sl2 - m) of one 64-key tile for this lane's 32 scores, in bf16 for the PV
@@ -705,7 +719,6 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
       for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(qf[t]));
       asm volatile("" ::"v"(qblk));
       if constexpr (BAND_B) asm volatile("" ::"v"(qpos));
-      auto entry = [&](int t) { return t < nt ? sm.win_e[t] : -1; };
 
       // Prologue: tiles 0 .. lead-1 issued; this wave waits for all of them but the last
       // (group A: tile 0; group B: tiles 0 and 1), then tile 0 is published.
@@ -924,25 +937,39 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         a.lse[(int64_t)(it.q0 + pe) * a.Hq + (int64_t)it.g * G + he] = lse2 * kLn2;
       }
     } else {
-      f32x4 y[NDB][4];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {         // 32 fp32 values per row and pass
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
-          *(f32x4*)&ep[ep_slot(ecol, 2 * v4 + ehl)] = x;
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int k = 0; k < 4; ++k) y[db][k] = *(const f32x4*)&ep[ep_slot(8 * k + (ln >> 3), ec)];
-        asm volatile("" ::: "memory");
-      }
+      // A split piece: fp16 partial rows (piece_factor) through the same staging.
+      float amax = 0.f;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(o[db][v]));
+      float restore;
+      const float mul = piece_factor(amax, inv, &restore);
+      f16x8 y[NDB / 2][4];
+#pragma unroll
+      for (int pb = 0; pb < NDB / 2; ++pb) {     // 64 fp16 values per row and pass
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x16& ob16 = o[2 * pb + j];
+            f32x4 x = {ob16[4 * v4] * mul, ob16[4 * v4 + 1] * mul, ob16[4 * v4 + 2] * mul, ob16[4 * v4 + 3] * mul};
+            *(f16x4*)&ep[ep_slot(ecol, 4 * j + v4) + 2 * ehl] = __builtin_convertvector(x, f16x4);
+          }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[pb][k] = *(const f16x8*)&ep[ep_slot(8 * k + (ln >> 3), ec)];
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int pb = 0; pb < NDB / 2; ++pb)
+#pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (brow[k] >= 0) *(f32x4*)(a.part_o + (int64_t)brow[k] * HD + 32 * db + 4 * ec) = y[db][k];
-      if (qvalid && ehl == 0) a.part_lse[pslot * kRowsPerWG + wave * 32 + ecol] = lse2;
+          if (brow[k] >= 0) *(f16x8*)(a.part_h + (int64_t)brow[k] * HD + 64 * pb + 8 * ec) = y[pb][k];
+      if (qvalid && ehl == 0) {
+        a.part_lse[pslot * kRowsPerWG + wave * 32 + ecol] = lse2;
+        a.part_scale[pslot * kRowsPerWG + wave * 32 + ecol] = restore;
+      }
     }
 
     if (a.stats && tid == 0) {
@@ -1298,6 +1325,15 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
     const float lt = l + __shfl_xor(l, 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+    float prestore = 1.f, pmul = inv;
+    if (pslot >= 0) {   // uniform; both lane halves of a row take part in the row's maximum
+      float amax = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(o[db][v]));
+      pmul = piece_factor(amax, inv, &prestore);
+    }
     if (qvalid && team == 0) {
       if (pslot < 0) {
         const int64_t row = (int64_t)(it.q0 + pos) * a.Hq + (int64_t)it.g * G + hh;
@@ -1311,15 +1347,19 @@ __global__ __launch_bounds__(kNThreads) void attn_bf16_narrow_kernel(AttnArgs a)
           }
         if (hl == 0 && a.lse) a.lse[row] = lse2 * kLn2;
       } else {
-        float* pp = a.part_o + ((int64_t)pslot * kRowsPerWG + rho) * HD + 4 * hl;
+        // A split piece: fp16 partial row (piece_factor, taken for every lane above).
+        uint16_t* pp = a.part_h + ((int64_t)pslot * kRowsPerWG + rho) * HD + 4 * hl;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
-            f32x4 x = {o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv, o[db][4 * v4 + 3] * inv};
-            *(f32x4*)(pp + 32 * db + 8 * v4) = x;
+            f32x4 x = {o[db][4 * v4] * pmul, o[db][4 * v4 + 1] * pmul, o[db][4 * v4 + 2] * pmul, o[db][4 * v4 + 3] * pmul};
+            *(f16x4*)(pp + 32 * db + 8 * v4) = __builtin_convertvector(x, f16x4);
           }
-        if (hl == 0) a.part_lse[(int64_t)pslot * kRowsPerWG + rho] = lse2;
+        if (hl == 0) {
+          a.part_lse[(int64_t)pslot * kRowsPerWG + rho] = lse2;
+          a.part_scale[(int64_t)pslot * kRowsPerWG + rho] = prestore;
+        }
       }
     }
     if (a.stats && (tid & 127) == 0) {   // the first wave of each team, for its tiles

@@ -155,7 +155,9 @@ struct AttnArgs {
   const void* v_cache;
   void* out;
   float* lse;
-  float* part_o;          // [kMaxPartialSlots][256][d] normalized partial outputs
+  float* part_o;          // [kMaxPartialSlots][256][d] normalized partial outputs (fp32 steps)
+  uint16_t* part_h;       // the same in fp16 (bf16 steps), each row scaled by part_scale's inverse
+  float* part_scale;      // [kMaxPartialSlots][256] factor that restores an fp16 partial row
   float* part_lse;        // [kMaxPartialSlots][256] log2-domain partial LSE (slot = piece)
   const int32_t* cu_q;
   const int32_t* kv_len;

@@ -5,7 +5,9 @@
 // softmax over the union of the chunks is their lse-weighted mean:
 //   M = max_c lse_c,  w_c = 2^(lse_c - M),  O = sum_c w_c O_c / sum_c w_c,
 //   lse = M + log2(sum_c w_c).
-// This is the same online-softmax identity the attention kernel applies tile by tile.
+// This is the same online-softmax identity the attention kernel applies tile by tile. For
+// bf16 steps the attention kernels store O_c in fp16, each row multiplied by a power of two
+// that keeps it in range, and the factor that undoes it beside the LSE.
 #include "bcp_internal.h"
 
 namespace bcp {
@@ -13,6 +15,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 constexpr float kLn2 = 0.69314718055994531f;
 
 template <int HD, bool BF16_OUT>
@@ -49,6 +52,15 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     if (w >= plan[kHdrSplit] * ngrp) break;
     const int s = u / a.nqt, r = u - (u / a.nqt) * a.nqt;
     const int rho = grp * RPW + rr;
+    // Partial row of one piece: fp32 for fp32 steps; for bf16 steps fp16 values times the
+    // row's restoring factor.
+    auto partial = [&](int64_t slot) -> f32x4 {
+      const int64_t row = slot * kRowsPerWG + rho;
+      if constexpr (BF16_OUT)
+        return __builtin_convertvector(*(const f16x4*)(a.part_h + row * HD + 4 * d4), f32x4) * a.part_scale[row];
+      else
+        return *(const f32x4*)(a.part_o + row * HD + 4 * d4);
+    };
     float lc[MAXC];
     f32x4 oc[MAXC];
 #pragma unroll
@@ -58,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
       if (k < n) {
         const int64_t slot = ps0 + k;
         lc[k] = a.part_lse[slot * kRowsPerWG + rho];
-        oc[k] = *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+        oc[k] = partial(slot);
       }
     }
     int q0, q_len;
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
       for (int c = MAXC; c < n; ++c) {
         const int64_t slot = ps0 + c;
         const float wc = __builtin_amdgcn_exp2f(a.part_lse[slot * kRowsPerWG + rho] - M);
-        acc += wc * *(const f32x4*)(a.part_o + (slot * kRowsPerWG + rho) * HD + 4 * d4);
+        acc += wc * partial(slot);
         wsum += wc;
       }
       acc *= 1.f / wsum;
