@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--live-in-cache", action="store_true",
                    help="live keys/values already in the pool at kv_len + i: attention reads one "
                         "paged source and the commit moves only block ids")
-    p.add_argument("--also", default="4,5",
+    p.add_argument("--also", default="4,5,6,3",
                    help="comma-separated workloads whose attention call is also timed (cold, with its "
                         "own roofline) on the default line; '' for none")
     p.add_argument("--also-steps", type=int, default=20, help="timed calls per --also workload")
