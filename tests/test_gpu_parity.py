@@ -554,14 +554,15 @@ def _plan_words(case, dc):
 
 @pytest.mark.parametrize("vexp", [26, -100], ids=["values_2e26", "values_2e-100"])
 @pytest.mark.parametrize("q_lens", [[64, 64], [9, 5]], ids=["wide", "narrow"])
-def test_split_partials_keep_the_value_scale(vexp, q_lens):
+@pytest.mark.parametrize("d", [128, 64])
+def test_split_partials_keep_the_value_scale(vexp, q_lens, d):
     """Split pieces store their partial rows in 16 bits, each row scaled by a power of two into
     range: outputs reaching 5e5 (past fp16's largest value) and of order 1e-32 (far below its
     smallest) come back at their scale. The step is cut into split pieces (checked in the
     plan header), and the result is compared scale-free with the oracle."""
     rng = np.random.default_rng(40 + abs(vexp))
-    case = make_case(40, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64,
-                     page_size=16, q_lens=q_lens, kv_lens=[1500, 900], qkv_std=1 / np.sqrt(128), rng=rng)
+    case = make_case(40, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=d, block_size=64,
+                     page_size=16, q_lens=q_lens, kv_lens=[1500, 900], qkv_std=1 / np.sqrt(d), rng=rng)
     f = np.float32(2.0 ** vexp)
     case.v_new = bf16_bits(bf16_float(case.v_new) * f)
     case.v_cache = bf16_bits(bf16_float(case.v_cache) * f)   # NaN slots stay NaN
