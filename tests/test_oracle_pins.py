@@ -501,6 +501,29 @@ def test_large_scores_rescale_path():
                                atol=1e-11)
 
 
+def test_score_shift_changes_only_the_lse():
+    """Adding c*e0 to every key, cached and live, adds scale*c*q[i,h,0] to every score of
+    query row (i, h): a constant per row, so the softmax is unchanged and the natural-log LSE
+    moves by exactly that constant. With c = 1024 and inputs on a 1/64 grid the shifted keys
+    are exact in float32, and the shifts (past 800 natural-log units, beyond where exp
+    overflows or underflows even in float64) test the oracle's stability."""
+    rng = np.random.default_rng(61)
+    c, _ = contiguous_case(rng, q_len=40, kv_len=90, Hq=4, Hkv=2, d=16, D=16, P=8, std=2.0)
+    for k in ("q", "k_new", "v_new", "k_cache", "v_cache"):
+        c[k] = np.where(np.isfinite(c[k]), np.round(c[k] * 64) / 64, c[k]).astype(np.float32)
+    O, L = run(c, scale=0.25)
+    shifted = dict(c)
+    shifted["k_new"] = c["k_new"].copy()
+    shifted["k_new"][..., 0] += 1024.0
+    shifted["k_cache"] = c["k_cache"].copy()
+    shifted["k_cache"][..., 0] += 1024.0         # NaN slots stay NaN and are never read
+    O2, L2 = run(shifted, scale=0.25)
+    shift = 0.25 * 1024.0 * c["q"][..., 0].astype(np.float64)
+    assert np.abs(shift).max() > 800             # exp overflows float64 past ~709
+    np.testing.assert_allclose(O2, O, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(L2 - L, shift, rtol=0, atol=1e-9)
+
+
 def test_workload_shapes():
     """The named workloads have the stated shapes (cheap structural checks)."""
     c1 = config(1)
